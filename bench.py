@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+One step = the whole decode path for one batch: slot mapping of each sequence's
+newest token, the cache write of its K/V row, the paged attention partition pass
+and (when the context is split) the reduce pass.  Several independently seeded
+batches of the same shape are resident and steps rotate over them, so a timed
+step never re-reads a pool that an earlier step left in the 256 MB Infinity
+Cache.  Inputs are synthetic (seeded N(0,1) values with the workload's shapes).
+
+Prints one JSON line:
+  value        = KV bytes the method must read per step / step time, GB/s
+  roofline     = the partition kernel alone, timed with HIP events on its stream
+  cpu_baseline = the float64 oracle on the host, on a bounded sample of the batch
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: KV-read HBM GB/s (% of peak) + seq-steps/sec, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+KV_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload 1-4 (decode)")
+    ap.add_argument("--replicas", type=int, default=0, help="resident batches to rotate (0: enough for >= 1.2 GB)")
+    ap.add_argument("--partition", type=int, default=None, help="partition tokens (default: workload's, else auto)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", type=str, default=None, help="JSON file with measured HBM bytes per launch")
+    return ap.parse_args()
+
+
+class Batch:
+    """One resident batch: pools filled up to each sequence's previous token, and the
+    arguments of every call of a step, prepared once."""
+
+    def __init__(self, w, partition, pa, torch, to_dev):
+        from workloads import POISON_BITS, queries, write_plan
+
+        dev = "cuda:0"
+        self.w = w
+        self.tables = torch.from_numpy(w.block_tables).to(dev)
+        self.lens = torch.from_numpy(w.context_lens).to(dev)
+        shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        ints = {"f32": torch.int32, "bf16": torch.int16, "e5m2": torch.uint8}[w.kv_dtype]
+        store = {"f32": torch.float32, "bf16": torch.bfloat16, "e5m2": torch.uint8}[w.kv_dtype]
+        self.pk = torch.full(shape, POISON_BITS[w.kv_dtype], dtype=ints, device=dev).view(store)
+        self.pv = self.pk.clone()
+        hist = write_plan(w, "cached")
+        slots = pa.slot_mapping(torch.from_numpy(hist.cu).to(dev), torch.from_numpy(hist.end_pos).to(dev),
+                                self.tables, hist.num_tokens, w.num_blocks)
+        pa.kv_cache_write(to_dev(hist.k, w.src_dtype), to_dev(hist.v, w.src_dtype), self.pk, self.pv, slots)
+        new = write_plan(w, "new")
+        self.cu = torch.from_numpy(new.cu).to(dev)
+        self.end = torch.from_numpy(new.end_pos).to(dev)
+        self.knew = to_dev(new.k, w.src_dtype)
+        self.vnew = to_dev(new.v, w.src_dtype)
+        self.ntok = new.num_tokens
+        self.slots = torch.empty(self.ntok, dtype=torch.int32, device=dev)
+        self.q = to_dev(queries(w), w.q_dtype)
+        self.out = torch.empty_like(self.q)
+        g = w.gqa_group
+        self.partition = partition
+        need = pa.workspace_size(w.num_seqs, w.num_kv_heads, g, w.head_dim, w.max_context_len, partition)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self.resolved = partition if partition >= 0 else pa.auto_partition(w.num_seqs, w.num_kv_heads, g, w.head_dim,
+                                                                            w.max_context_len)
+        self.split = need > 0
+        qd = pa.binding.dtype_code(self.q)
+        kd = pa.binding.dtype_code(self.pk)
+        sd = pa.binding.dtype_code(self.knew)
+        n, hkv, d, bs, nb = w.num_seqs, w.num_kv_heads, w.head_dim, w.block_size, w.num_blocks
+        mb, ml = w.max_blocks_per_seq, w.max_context_len
+        P = lambda t: t.data_ptr()
+        self.args_slot = (P(self.slots), P(self.cu), P(self.end), P(self.tables), mb, n, self.ntok, bs, nb)
+        self.args_write = (P(self.knew), P(self.vnew), P(self.pk), P(self.pv), P(self.slots), self.ntok, hkv, d, bs,
+                           nb, sd, kd)
+        self.args_parts = (P(self.out), P(self.q), P(self.pk), P(self.pv), P(self.tables), mb, P(self.lens), n, hkv, g,
+                           d, bs, nb, ml, w.scale, qd, kd, partition, P(self.ws), self.ws.numel())
+        self.args_reduce = (P(self.out), P(self.lens), mb, n, hkv, g, d, bs, ml, qd, kd, partition, P(self.ws),
+                            self.ws.numel())
+        self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * d * 2 * KV_BYTES[w.kv_dtype]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path needs no second GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_251_amd as pa
+    from workloads import CONFIG_NAMES, make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lib = pa.lib()
+
+    def to_dev(raw, dtype):
+        if dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(raw, np.float32)).to("cuda:0")
+        return torch.from_numpy(np.ascontiguousarray(raw, np.uint16).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+
+    w0 = make_config(args.config)
+    assert w0.is_decode, "bench.py times the decode workloads (1-4)"
+    partition = args.partition if args.partition is not None else (w0.partition_size or -1)
+    pool_bytes = w0.num_blocks * w0.num_kv_heads * 16 * w0.head_dim * 2 * KV_BYTES[w0.kv_dtype]
+    reps = args.replicas or max(2, min(8, -(-1_200_000_000 // pool_bytes)))
+    t_setup = time.perf_counter()
+    batches = [Batch(w0 if r == 0 else make_config(args.config, replica=r), partition, pa, torch, to_dev)
+               for r in range(reps)]
+    torch.cuda.synchronize()
+    print(f"# setup: {reps} resident batches of {CONFIG_NAMES[args.config]} in {time.perf_counter() - t_setup:.1f} s",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def check(st, fn):
+        if st != 0:
+            raise RuntimeError(f"{fn}: {lib.pa_last_error().decode()}")
+
+    def step(b, ev=None):
+        check(lib.paged_kv_slot_mapping(*b.args_slot, sh), "slot mapping")
+        check(lib.kv_cache_write(*b.args_write, sh), "cache write")
+        if ev is not None:
+            ev[0].record(stream)
+        check(lib.paged_attention_decode_partitions(*b.args_parts, sh), "decode partitions")
+        if ev is not None:
+            ev[1].record(stream)
+        if b.split:
+            check(lib.paged_attention_decode_reduce(*b.args_reduce, sh), "decode reduce")
+
+    for i in range(args.warmup):
+        step(batches[i % reps])
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(batches[i % reps], evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = float(np.mean(kern_ms))
+    step_bytes = float(np.mean([batches[i % reps].kv_bytes for i in range(args.steps)]))
+    seqs = w0.num_seqs
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    kern_gbs = step_bytes / (kern_avg * 1e-3) / 1e9
+
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(CONFIG_NAMES[args.config])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(batches[0].w, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w0.kv_dtype if w0.kv_dtype == w0.q_dtype else f"{w0.q_dtype}-q/{w0.kv_dtype}-kv",
+        "data": "synthetic",
+        "config": {
+            "workload": CONFIG_NAMES[args.config],
+            "num_seqs": seqs,
+            "num_q_heads": w0.num_q_heads,
+            "num_kv_heads": w0.num_kv_heads,
+            "head_dim": w0.head_dim,
+            "block_size": w0.block_size,
+            "context_lens": f"{int(w0.context_lens.min())}..{int(w0.context_lens.max())}",
+            "partition_tokens": batches[0].resolved,
+            "resident_batches": reps,
+            "step": "slot mapping + cache write (newest token) + decode partitions" +
+                    (" + reduce" if batches[0].split else ""),
+        },
+        "seq_steps_per_s": round(seqs / (ms_step * 1e-3), 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": int(step_bytes),
+        "wall_s": round(wall, 4),
+        "roofline": {
+            "kernel": "decode_partition_kernel",
+            "bound": "hbm",
+            "achieved": round(kern_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(kern_avg * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(step_bytes),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(w, budget_s):
+    """Time the oracle (as it stands) on the host: each pass takes the next sequences of
+    the batch through the oracle's slot mapping, cache write of the newest token and
+    paged decode, until the time budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import POISON_BITS, queries, write_plan
+
+    q = queries(w)
+    done_seqs, done_bytes, t_used = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        s0 = 0
+        while t_used < budget_s and s0 < w.num_seqs:
+            sel = list(range(s0, min(s0 + 8, w.num_seqs)))
+            # history of these sequences (not timed: it is the state the step starts from)
+            pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                 POISON_BITS[w.kv_dtype])
+            pv = pk.copy()
+            hist = write_plan(w, "cached", sel)
+            hs = oracle.slot_mapping(w.block_tables, hist.counts, hist.end_pos, w.block_size)
+            oracle.cache_write(pk, hist.k, hs, w.src_dtype, w.kv_dtype, w.block_size)
+            oracle.cache_write(pv, hist.v, hs, w.src_dtype, w.kv_dtype, w.block_size)
+            new = write_plan(w, "new", sel)
+            t0 = time.perf_counter()
+            ns = oracle.slot_mapping(w.block_tables, new.counts, new.end_pos, w.block_size)
+            oracle.cache_write(pk, new.k, ns, w.src_dtype, w.kv_dtype, w.block_size)
+            oracle.cache_write(pv, new.v, ns, w.src_dtype, w.kv_dtype, w.block_size)
+            oracle.paged_decode(pk, pv, w.kv_dtype, q, w.q_dtype, w.block_tables, w.context_lens, w.block_size,
+                                w.scale, seqs=sel)
+            t_used += time.perf_counter() - t0
+            done_seqs += len(sel)
+            done_bytes += int(w.context_lens[sel].astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 2 * \
+                KV_BYTES[w.kv_dtype]
+            s0 += 8
+    return {
+        "value": round(done_bytes / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "seq_steps_per_s": round(done_seqs / t_used, 3),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {done_seqs} of {w.num_seqs} sequences of the timed workload, one decode step each "
+                  f"(slot mapping, cache write of the newest token, float64 attention), {t_used:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    main()

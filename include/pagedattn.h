@@ -1,0 +1,220 @@
+/*
+ * libpagedattn -- PagedAttention over a blocked KV cache, for AMD MI355X (gfx950).
+ *
+ * The operations follow these pages (cited by title and section):
+ *   [CI]  Colossal-Inference release post ("AI大模型推理速度翻倍，Colossal-Inference开源发布"),
+ *         sections "分块式KV缓存 (BlockedKeyValueCache)", "KV缓存量化 (KVCache Quant)",
+ *         "分页注意力算法 (PagedAttention)", "连续批量化算法 (Continuous Batching)".
+ *   [OPT] LLM inference optimisation overview ("AI 大模型推理优化技术详解"),
+ *         sections 2.1.2 "Paged Attention", 2.2.1 "Flash Attention", 2.2.2 "GQA".
+ *
+ * Data model
+ *   Every sequence's keys and values live in fixed-size blocks of `block_size`
+ *   tokens taken from a shared pool; a per-sequence block table maps logical
+ *   block j (tokens j*B .. j*B+B-1) to a physical block id [CI BlockedKeyValueCache,
+ *   OPT 2.1.2].  Several tables may name the same physical block (a shared prefix).
+ *
+ *   Pool layout (key and value pools alike), row-major:
+ *       cache[num_blocks][num_kv_heads][block_size][head_dim]
+ *   so one (block, kv head) tile of block_size x head_dim elements is contiguous.
+ *
+ *   Query head h reads KV head h / gqa_group  [OPT 2.2.2; the grouping is taken
+ *   as contiguous].  num_q_heads = num_kv_heads * gqa_group.
+ *   Queries and outputs are row-major [rows][num_q_heads][head_dim].
+ *
+ * Element types
+ *   PA_F32   IEEE binary32
+ *   PA_BF16  bfloat16 (upper half of a binary32); outputs are rounded to nearest even
+ *   PA_FP8_E5M2  1 sign, 5 exponent (bias 15), 2 mantissa bits, with inf and NaN; the
+ *            cache write casts bf16 -> E5M2 by round-to-nearest-even without saturation
+ *            (|x| >= 61440 -> inf, NaN -> sign|0x7F); reads widen exactly
+ *            [CI KVCache Quant: cast on store, cast back on load].
+ *
+ * Conventions for every entry point
+ *   - All pointers are device pointers unless stated; the caller owns every buffer.
+ *     The library never allocates or frees device memory, never synchronises, keeps
+ *     no state besides a thread-local error string, and is re-entrant.
+ *   - Work is enqueued on `stream`; calls return before the device has finished.
+ *   - Scalar arguments and pointer alignment are checked on the host before anything
+ *     is enqueued: a bad value returns PA_ERR_INVALID_ARGUMENT, a well-formed but
+ *     unsupported combination PA_ERR_UNSUPPORTED, and nothing is launched.  A launch
+ *     failure returns PA_ERR_DEVICE.  pa_last_error() gives the reason in words.
+ *   - Device contents (table entries, lengths, slots) are not validated on the host.
+ *     Kernels stay in bounds regardless: a table entry outside [0, num_blocks), a
+ *     slot outside the pool or a position past the table is skipped (its token
+ *     contributes nothing / its row is not written); context lengths are clamped to
+ *     [0, min(max_context_len, max_blocks_per_seq * block_size)].  Results for such
+ *     inputs are unspecified but no access leaves the buffers described here.
+ *   - Supported now: block_size 16; head_dim 64 or 128; gqa_group 1, 2, 4, 8 or 16;
+ *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,
+  PA_ERR_UNSUPPORTED = 2,
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_DEVICE = 4
+} pa_status_t;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E5M2 = 2 } pa_dtype_t;
+
+/* Version of this header's ABI (PA_ABI_VERSION). */
+int pa_abi_version(void);
+
+/* Static text naming a status code. */
+const char* pa_status_string(pa_status_t status);
+
+/* Reason for the last failing call on this host thread ("" after a success).  The
+ * string stays valid until the next call on the same thread. */
+const char* pa_last_error(void);
+
+/*
+ * paged_kv_slot_mapping -- the pool slot of every packed token row.
+ * [CI BlockedKeyValueCache: logical blocks reach physical blocks through the block
+ *  table; OPT 2.1.2: block size 16 by default]
+ *
+ * Sequence s owns packed rows cu_tokens[s] .. cu_tokens[s+1]-1 (n_s rows); row i of
+ * them is the token at logical position p = end_pos[s] - n_s + i, and
+ *     slot_mapping[row] = block_tables[s][p / block_size] * block_size + p % block_size.
+ * A row whose position is negative or past the table, or whose table entry is not in
+ * [0, num_blocks), gets -1 (a cache write skips it).  Rows not covered by
+ * cu_tokens[0] .. cu_tokens[num_seqs] also get -1.
+ *
+ *   slot_mapping  out, int32 [num_tokens]
+ *   cu_tokens     int32 [num_seqs + 1], non-decreasing, cu_tokens[0] = 0
+ *   end_pos       int32 [num_seqs]: one past the last written position of each sequence
+ *                 (the context length when the rows are a step's newest tokens)
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   num_blocks * block_size must be below 2^31.
+ */
+pa_status_t paged_kv_slot_mapping(int32_t* slot_mapping, const int32_t* cu_tokens,
+                                  const int32_t* end_pos, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, int32_t num_seqs,
+                                  int32_t num_tokens, int32_t block_size, int32_t num_blocks,
+                                  hipStream_t stream);
+
+/*
+ * kv_cache_write -- scatter new key/value rows into the pools ("kernel 1").
+ * [CI BlockedKeyValueCache; CI KVCache Quant: the writer casts to E5M2 on store]
+ *
+ *   key, value    [num_tokens][num_kv_heads][head_dim] of src_dtype, dense, 16-byte
+ *                 aligned
+ *   key_cache,
+ *   value_cache   [num_blocks][num_kv_heads][block_size][head_dim] of cache_dtype
+ *   slot_mapping  int32 [num_tokens]; row r goes to block slot/block_size, offset
+ *                 slot % block_size; slot < 0 or >= num_blocks*block_size skips the row
+ *   (src, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2)}; a same-type write
+ *   copies bits, the E5M2 cast is round-to-nearest-even (see above).
+ *   Two rows with the same slot in one call race: the stored row is unspecified.
+ */
+pa_status_t kv_cache_write(const void* key, const void* value, void* key_cache,
+                           void* value_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, pa_dtype_t src_dtype, pa_dtype_t cache_dtype,
+                           hipStream_t stream);
+
+/*
+ * paged_attention_workspace_size -- bytes of device workspace that
+ * paged_attention_decode / paged_attention_varlen need for these arguments
+ * (0 when no sequence is split).  `partition_size` as in paged_attention_decode
+ * (-1 resolves the same way the attention call will).
+ *
+ * Workspace layout (float32), with P = partitions per sequence and R = num_seqs:
+ *   o  [R][num_q_heads][P][head_dim]   partition outputs, already divided by l
+ *   m  [R][num_q_heads][P]             partition max of scale*log2(e)*q.k
+ *   l  [R][num_q_heads][P]             partition sum of 2^(score - m)
+ */
+size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                      int32_t gqa_group, int32_t head_dim,
+                                      int32_t max_context_len, int32_t partition_size);
+
+/* The partition size (tokens) that partition_size = -1 resolves to. */
+int32_t paged_attention_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t gqa_group, int32_t head_dim,
+                                       int32_t max_context_len);
+
+/*
+ * paged_attention_decode -- single-token decode attention over the blocked cache
+ * ("kernel 2").  [CI PagedAttention: decode attention is a memory-bound GEMV over the
+ * cached keys and values, read block by block through the table; OPT 2.2.2 GQA;
+ * OPT 2.2.1: softmax reduced without the whole input, used for split-KV]
+ *
+ * For sequence s with L = context_lens[s] (the current token included) and query
+ * head h (KV head g = h / gqa_group):
+ *   S_t = scale * q[s][h] . K_s[t][g],   t < L
+ *   out[s][h] = sum_t exp(S_t - max S) V_s[t][g] / sum_t exp(S_t - max S)
+ * where K_s[t] is row t % block_size of physical block block_tables[s][t / block_size].
+ * L = 0 gives a zero row.
+ *
+ *   out           [num_seqs][num_kv_heads*gqa_group][head_dim], q_dtype
+ *   query         [num_seqs][num_kv_heads*gqa_group][head_dim], q_dtype, 16-byte aligned
+ *   key_cache,
+ *   value_cache   pools as above, kv_dtype
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entries past ceil(L/B) unread
+ *   context_lens  int32 [num_seqs]
+ *   max_context_len  host-side upper bound of context_lens (sizes the launch)
+ *   partition_size   0: one pass over each whole context; > 0 (multiple of block_size):
+ *                    split every context into partitions of that many tokens, each
+ *                    written to the workspace and merged by a second kernel;
+ *                    -1: chosen by the library (paged_attention_auto_partition)
+ *   workspace     device buffer of at least paged_attention_workspace_size(...) bytes
+ *                 (may be NULL when that size is 0), 256-byte aligned; its contents
+ *                 are scratch, overwritten on every call
+ */
+pa_status_t paged_attention_decode(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_context_len, float scale, pa_dtype_t q_dtype,
+                                   pa_dtype_t kv_dtype, int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two passes of paged_attention_decode, for callers that schedule or time them
+ * apart.  Called one after the other on one stream with the same arguments they are
+ * exactly paged_attention_decode.
+ *
+ * paged_attention_decode_partitions -- the streaming pass.  Every sequence with at most
+ *   one partition gets its output row; every split sequence gets, per query head and
+ *   partition, the partition's normalised output, max and sum in the workspace (layout
+ *   above).  [CI PagedAttention; OPT 2.2.1]
+ * paged_attention_decode_reduce -- the merge pass of split-KV: for each split sequence
+ *   and query head, M = max_j m_j, w_j = 2^(m_j - M) l_j, out = sum_j w_j o_j / sum_j w_j
+ *   (the running max / sum identity of OPT 2.2.1).  Does nothing when no sequence is
+ *   split.  Arguments mean what they mean in paged_attention_decode.
+ */
+pa_status_t paged_attention_decode_partitions(void* out, const void* query, const void* key_cache,
+                                              const void* value_cache, const int32_t* block_tables,
+                                              int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                              int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                              int32_t max_context_len, float scale, pa_dtype_t q_dtype,
+                                              pa_dtype_t kv_dtype, int32_t partition_size, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream);
+
+pa_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens, int32_t max_blocks_per_seq,
+                                          int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                                          int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                          pa_dtype_t q_dtype, pa_dtype_t kv_dtype, int32_t partition_size,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

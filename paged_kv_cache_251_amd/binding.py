@@ -1,0 +1,190 @@
+"""ctypes binding of libpagedattn (include/pagedattn.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels on the
+caller's current torch stream.  Torch supplies device memory and the stream
+handle.  There is no fallback: if the shared library is missing this module
+raises on first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_F32, PA_BF16, PA_FP8_E5M2 = 0, 1, 2
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "device error"}
+
+_i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes), in header order
+SIGNATURES = {
+    "pa_abi_version": (ctypes.c_int, []),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "paged_kv_slot_mapping": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "kv_cache_write": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                      ctypes.c_int, _vp]),
+    "paged_attention_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attention_auto_partition": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "paged_attention_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _i32, _vp, _sz, _vp]),
+    "paged_attention_decode_partitions": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                                         _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
+                                                         _i32, _vp, _sz, _vp]),
+    "paged_attention_decode_reduce": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                     ctypes.c_int, ctypes.c_int, _i32, _vp, _sz, _vp]),
+}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpagedattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing; build it with `python -m paged_kv_cache_251_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise PagedAttnError(fn, status, lib().pa_last_error().decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _expect(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _int32(*ts: torch.Tensor) -> None:
+    for t in ts:
+        _expect(t.dtype == torch.int32, f"index arrays must be int32, got {t.dtype}")
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e5m2):
+        return PA_FP8_E5M2
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def abi_version() -> int:
+    return lib().pa_abi_version()
+
+
+def slot_mapping(cu_tokens: torch.Tensor, end_pos: torch.Tensor, block_tables: torch.Tensor, num_tokens: int,
+                 num_blocks: int, block_size: int = 16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Pool slot of each packed token row (``paged_kv_slot_mapping``)."""
+    _dev(cu_tokens, end_pos, block_tables)
+    _int32(cu_tokens, end_pos, block_tables)
+    n = end_pos.shape[0]
+    _expect(cu_tokens.shape == (n + 1,) and block_tables.dim() == 2 and block_tables.shape[0] == n,
+            "cu_tokens [N+1], end_pos [N], block_tables [N, max_blocks]")
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int32, device=cu_tokens.device)
+    _dev(out)
+    _int32(out)
+    _expect(out.shape == (num_tokens,), "out must be [num_tokens]")
+    _check("paged_kv_slot_mapping", lib().paged_kv_slot_mapping(
+        _ptr(out), _ptr(cu_tokens), _ptr(end_pos), _ptr(block_tables), block_tables.shape[1], end_pos.shape[0],
+        num_tokens, block_size, num_blocks, _stream()))
+    return out
+
+
+def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                   slot_mapping: torch.Tensor) -> None:
+    """Scatter rows [T, Hkv, D] into the pools [num_blocks, Hkv, B, D] (``kv_cache_write``)."""
+    _dev(key, value, key_cache, value_cache, slot_mapping)
+    _int32(slot_mapping)
+    t, hkv, d = key.shape
+    nb, _, bs, _ = key_cache.shape
+    _expect(value.shape == key.shape and value.dtype == key.dtype, "key and value rows differ")
+    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    _expect(key_cache.shape[1] == hkv and key_cache.shape[3] == d, "rows and pools disagree on Hkv / D")
+    _expect(slot_mapping.shape == (t,), "slot_mapping must be [num_tokens]")
+    _check("kv_cache_write", lib().kv_cache_write(
+        _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), t, hkv, d, bs, nb,
+        dtype_code(key), dtype_code(key_cache), _stream()))
+
+
+def workspace_size(num_seqs: int, num_kv_heads: int, gqa_group: int, head_dim: int, max_context_len: int,
+                   partition_size: int = -1) -> int:
+    return int(lib().paged_attention_workspace_size(num_seqs, num_kv_heads, gqa_group, head_dim, max_context_len,
+                                                    partition_size))
+
+
+def auto_partition(num_seqs: int, num_kv_heads: int, gqa_group: int, head_dim: int, max_context_len: int) -> int:
+    return int(lib().paged_attention_auto_partition(num_seqs, num_kv_heads, gqa_group, head_dim, max_context_len))
+
+
+def alloc_workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int, scale: float,
+                           partition_size: int = -1, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention: query [N, Hq, D] against pools [nb, Hkv, 16, D] (``paged_attention_decode``)."""
+    _dev(query, key_cache, value_cache, block_tables, context_lens)
+    _int32(block_tables, context_lens)
+    n, hq, d = query.shape
+    nb, hkv, bs, _ = key_cache.shape
+    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    _expect(key_cache.shape[3] == d and hq % hkv == 0, "query and pools disagree on D / heads")
+    _expect(block_tables.dim() == 2 and block_tables.shape[0] == n and context_lens.shape == (n,),
+            "block_tables [N, max_blocks], context_lens [N]")
+    g = hq // hkv
+    if out is None:
+        out = torch.empty_like(query)
+    _dev(out)
+    _expect(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    need = workspace_size(n, hkv, g, d, max_context_len, partition_size)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = alloc_workspace(need, query.device)
+    _check("paged_attention_decode", lib().paged_attention_decode(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), n, hkv, g, d, bs, nb, max_context_len, scale, dtype_code(query),
+        dtype_code(key_cache), partition_size, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream()))
+    return out

@@ -1,0 +1,119 @@
+// Slot mapping and the cache write ("kernel 1") for gfx950.
+//
+// Colossal-Inference release post, "分块式KV缓存 (BlockedKeyValueCache)": logical blocks map
+// through a block table to physical blocks anywhere in the pool; "KV缓存量化 (KVCache
+// Quant)": the kernel that stores new keys and values casts them to FP8 E5M2 on the way.
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+
+// One thread per packed token row: find its sequence by binary search over cu, then
+// slot = table[p / B] * B + p % B for its logical position p.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(int32_t* __restrict__ slots,
+                                                           const int32_t* __restrict__ cu,
+                                                           const int32_t* __restrict__ end_pos,
+                                                           const int32_t* __restrict__ tables,
+                                                           int32_t max_blocks, int32_t num_seqs,
+                                                           int32_t num_tokens, int32_t block_size,
+                                                           int32_t num_blocks) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= num_tokens) return;
+  int lo = 0, hi = num_seqs;  // invariant: the answer is in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int a = cu[s], b = cu[s + 1];
+  int slot = -1;
+  if (t >= a && t < b) {
+    const int pos = end_pos[s] - (b - a) + (t - a);
+    const int lb = pos >= 0 ? pos / block_size : -1;
+    if (lb >= 0 && lb < max_blocks) {
+      const int phys = tables[(size_t)s * max_blocks + lb];
+      if (phys >= 0 && phys < num_blocks) slot = phys * block_size + pos % block_size;
+    }
+  }
+  slots[t] = slot;
+}
+
+hipError_t launch_slot_mapping(int32_t* slots, const int32_t* cu, const int32_t* end_pos,
+                               const int32_t* tables, int32_t max_blocks, int32_t num_seqs,
+                               int32_t num_tokens, int32_t block_size, int32_t num_blocks,
+                               hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int blocks = (num_tokens + 255) / 256;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(blocks), dim3(256), 0, stream, slots, cu, end_pos, tables,
+                     max_blocks, num_seqs, num_tokens, block_size, num_blocks);
+  return hipGetLastError();
+}
+
+// One thread per 16 source bytes of a row (4 f32 or 8 bf16 elements).  Source rows are
+// [token][kv_head][D]; destination [block][kv_head][B][D].
+template <int SRC, int DST>
+__global__ __launch_bounds__(256) void cache_write_kernel(const uint4* __restrict__ key, const uint4* __restrict__ value,
+                                                          uint8_t* __restrict__ key_cache,
+                                                          uint8_t* __restrict__ value_cache,
+                                                          const int32_t* __restrict__ slots, int32_t num_tokens,
+                                                          int32_t num_kv_heads, int32_t head_dim,
+                                                          int32_t block_size, int32_t num_blocks) {
+  constexpr int SRC_SZ = KvBytes<SRC>::value;
+  constexpr int EPC = 16 / SRC_SZ;  // elements per chunk
+  const int chunks_per_row = num_kv_heads * head_dim / EPC;
+  const size_t total = (size_t)num_tokens * chunks_per_row;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int t = (int)(i / chunks_per_row);
+  const int c = (int)(i % chunks_per_row);
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * block_size) return;
+  const int h = (c * EPC) / head_dim;
+  const int d = (c * EPC) % head_dim;
+  const size_t dst_elem = (((size_t)(slot / block_size) * num_kv_heads + h) * block_size + slot % block_size) *
+                              head_dim + d;
+  const uint4 kin = key[i];
+  const uint4 vin = value[i];
+  if constexpr (SRC == DST) {
+    *reinterpret_cast<uint4*>(key_cache + dst_elem * SRC_SZ) = kin;
+    *reinterpret_cast<uint4*>(value_cache + dst_elem * SRC_SZ) = vin;
+  } else {  // bf16 -> E5M2, 8 elements -> 8 bytes
+    auto cast8 = [](uint4 w) {
+      const uint32_t c0 = bf16_to_e5m2(w.x & 0xFFFFu) | (bf16_to_e5m2(w.x >> 16) << 8) |
+                          (bf16_to_e5m2(w.y & 0xFFFFu) << 16) | (bf16_to_e5m2(w.y >> 16) << 24);
+      const uint32_t c1 = bf16_to_e5m2(w.z & 0xFFFFu) | (bf16_to_e5m2(w.z >> 16) << 8) |
+                          (bf16_to_e5m2(w.w & 0xFFFFu) << 16) | (bf16_to_e5m2(w.w >> 16) << 24);
+      return make_uint2(c0, c1);
+    };
+    *reinterpret_cast<uint2*>(key_cache + dst_elem) = cast8(kin);
+    *reinterpret_cast<uint2*>(value_cache + dst_elem) = cast8(vin);
+  }
+}
+
+hipError_t launch_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                              const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, int src_kind,
+                              int cache_kind, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int src_sz = src_kind == KV_F32 ? 4 : 2;
+  const size_t total = (size_t)num_tokens * num_kv_heads * head_dim * src_sz / 16;
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  auto k = reinterpret_cast<const uint4*>(key);
+  auto v = reinterpret_cast<const uint4*>(value);
+  auto kc = reinterpret_cast<uint8_t*>(key_cache);
+  auto vc = reinterpret_cast<uint8_t*>(value_cache);
+  if (src_kind == KV_F32 && cache_kind == KV_F32)
+    hipLaunchKernelGGL((cache_write_kernel<KV_F32, KV_F32>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc, slots,
+                       num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+  else if (src_kind == KV_BF16 && cache_kind == KV_BF16)
+    hipLaunchKernelGGL((cache_write_kernel<KV_BF16, KV_BF16>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
+                       slots, num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+  else if (src_kind == KV_BF16 && cache_kind == KV_E5M2)
+    hipLaunchKernelGGL((cache_write_kernel<KV_BF16, KV_E5M2>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
+                       slots, num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pa

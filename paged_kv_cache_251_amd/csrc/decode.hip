@@ -1,0 +1,459 @@
+// Paged decode attention for gfx950: one work-group per (partition, KV head, sequence).
+//
+// What is computed (Colossal-Inference release post, "分页注意力算法 (PagedAttention)":
+// decode attention is a memory-bound GEMV over the cached keys and values, read block by
+// block through the block table; LLM inference optimisation overview, 2.2.2 "GQA": the
+// query heads of a group share one KV head; 2.2.1 "Flash Attention": softmax reduced
+// without the whole input, which is what lets a context be split into partitions):
+//   out[s][h] = sum_t 2^(S_t - M) V[t][g] / sum_t 2^(S_t - M),  S_t = scale*log2(e) q[s][h].K[t][g]
+//
+// Mapping onto CDNA4 (wave64):
+//  * A KV tile (one physical block, one KV head) is block_size x head_dim contiguous
+//    elements.  A wave reads it with 4 coalesced loads; in each, 16-lane row r holds
+//    token 4i + r and lane c of the row holds head_dim/16 consecutive elements.
+//  * All G query heads of the group are kept in registers of every lane (only the
+//    lane's head_dim/16 slice), in a lane-dependent order that lets one pass of 4 DPP
+//    steps both finish the dot products and leave head h's score on lanes
+//    h*16/G .. h*16/G + 16/G - 1 of the row (row_reduce_heads).
+//  * Softmax state is kept per 16-lane row (its own tokens), so the loop needs no
+//    cross-row traffic.  The running max is only raised when a block's max exceeds it
+//    by more than TAU (2^8): exact, since the same stale max is used for the numerator
+//    and the denominator, and it makes the rescale branch rare.
+//  * Probabilities reach the PV lanes by DPP row broadcast; V is accumulated in fp32
+//    (f32 / bf16 caches) or with f16 dot2 over token pairs (E5M2 cache, whose codes
+//    widen exactly to f16).
+//  * Rows, then waves, are merged at the end; a single partition writes the output,
+//    several write (o/l, m, l) to the workspace for the reduce kernel.
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+
+constexpr float TAU = 8.0f;
+
+template <int G>
+__device__ __forceinline__ float bcast_head(float v, int h) {
+  switch (h * (16 / G)) {
+#define PA_C(n) \
+  case n:       \
+    return row_bcast<n>(v);
+    PA_C(0) PA_C(1) PA_C(2) PA_C(3) PA_C(4) PA_C(5) PA_C(6) PA_C(7)
+    PA_C(8) PA_C(9) PA_C(10) PA_C(11) PA_C(12) PA_C(13) PA_C(14) PA_C(15)
+#undef PA_C
+  }
+  return v;
+}
+template <int G>
+__device__ __forceinline__ uint32_t bcast_head_u32(uint32_t v, int h) {
+  switch (h * (16 / G)) {
+#define PA_C(n) \
+  case n:       \
+    return row_bcast_u32<n>(v);
+    PA_C(0) PA_C(1) PA_C(2) PA_C(3) PA_C(4) PA_C(5) PA_C(6) PA_C(7)
+    PA_C(8) PA_C(9) PA_C(10) PA_C(11) PA_C(12) PA_C(13) PA_C(14) PA_C(15)
+#undef PA_C
+  }
+  return v;
+}
+
+template <int KV, int D, int G>
+struct DecodeTile {
+  static constexpr int SZ = KvBytes<KV>::value;
+  static constexpr int EPL = D / 16;          // elements per lane per token row
+  static constexpr int NDW = EPL * SZ / 4;    // dwords per lane per token row
+  static constexpr int NL = 4;                // loads per 16-token tile (4 rows each)
+  static constexpr int QDW = KV == KV_F32 ? EPL : EPL / 2;  // q dwords per head per lane
+};
+
+template <int KV, int D, int G, int W>
+__global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodeParams p) {
+  using T = DecodeTile<KV, D, G>;
+  constexpr int EPL = T::EPL, NDW = T::NDW, NL = T::NL, QDW = T::QDW, SZ = T::SZ;
+  constexpr int S = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = lane >> 4, col = lane & 15;
+  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int hq = p.num_kv_heads * G;
+
+  int qrow = s;
+  if (p.cu_q != nullptr) {  // packed varlen batch: this kernel serves the 1-token rows
+    const int a = load_invariant(p.cu_q + s), b = load_invariant(p.cu_q + s + 1);
+    if (b - a != 1) return;
+    qrow = a;
+  }
+  int L = load_invariant(p.context_lens + s);
+  L = L < 0 ? 0 : L;
+  L = L > p.max_context_len ? p.max_context_len : L;
+  L = L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
+  int t0 = 0, t1 = L, nparts = 1;
+  if (p.partition_tokens > 0) {
+    t0 = part * p.partition_tokens;
+    t1 = min(L, t0 + p.partition_tokens);
+    nparts = (L + p.partition_tokens - 1) / p.partition_tokens;
+  }
+  if (part > 0 && t0 >= L) return;
+
+  // ---- the query group, in this lane's head order -------------------------------------
+  uint32_t qv[G][QDW];
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const int h = head_of_slot<G>(col, k);
+    const size_t qoff = ((size_t)qrow * hq + (size_t)g * G + h) * D + (size_t)col * EPL;
+    if constexpr (KV == KV_F32) {
+      load_dw<QDW>(qv[k], reinterpret_cast<const float*>(p.query) + qoff);
+    } else if constexpr (KV == KV_BF16) {
+      load_dw<QDW>(qv[k], reinterpret_cast<const uint16_t*>(p.query) + qoff);
+    } else {  // bf16 query against an E5M2 cache: widen to f16 pairs once
+      uint32_t raw[QDW];
+      load_dw<QDW>(raw, reinterpret_cast<const uint16_t*>(p.query) + qoff);
+#pragma unroll
+      for (int j = 0; j < QDW; ++j) qv[k][j] = pack_f16x2_rne(bf16lo(raw[j]), bf16hi(raw[j]));
+    }
+  }
+  // Consume the query registers here so that their load is waited for once, before the
+  // tile loop; otherwise the wait lands inside the loop and also drains the prefetch.
+#pragma unroll
+  for (int k = 0; k < G; ++k)
+#pragma unroll
+    for (int j = 0; j < QDW; ++j) asm volatile("" ::"v"(qv[k][j]));
+
+  float m_own = -__builtin_inff();  // running max (log2 domain) of this row's own head
+  float l_own = 0.f;                // running sum of 2^(S - m_own) over this row's tokens
+  float acc[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+
+  const int b_first = t0 / 16 + wave;
+  const int b_end = (t1 + 15) / 16;
+  const int* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const size_t tile_elems = (size_t)16 * D;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
+  const size_t lane_off = ((size_t)row * D + (size_t)col * EPL) * SZ;
+
+  auto load_tile = [&](int b, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW]) -> int {
+    int phys = load_invariant(table + b);
+    const bool ok = phys >= 0 && phys < p.num_blocks;
+    phys = ok ? phys : 0;
+    const size_t off = (((size_t)phys * p.num_kv_heads + g) * tile_elems) * SZ + lane_off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) load_dw<NDW>(kd[i], kbase + off + (size_t)i * 4 * D * SZ);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) load_dw<NDW>(vd[i], vbase + off + (size_t)i * 4 * D * SZ);
+    __builtin_amdgcn_sched_barrier(0);  // issue the tile before any math that follows
+    return ok;
+  };
+
+  auto compute_tile = [&](int b, bool ok, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW]) {
+    // valid tokens of this tile: [b*16, min(b*16+16, t1)), all of them if the block is valid
+    const int tok_lim = ok ? min(16, t1 - b * 16) : 0;
+    float sc[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float r[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        float a = 0.f;
+        if constexpr (KV == KV_F32) {
+#pragma unroll
+          for (int j = 0; j < EPL; ++j) a = fmaf(as_f32(qv[k][j]), as_f32(kd[i][j]), a);
+        } else if constexpr (KV == KV_BF16) {
+#pragma unroll
+          for (int j = 0; j < NDW; ++j) a = dot2_bf16(qv[k][j], kd[i][j], a);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NDW; ++j) {
+            a = dot2_f16(qv[k][2 * j], e5m2_pair_lo(kd[i][j]), a);
+            a = dot2_f16(qv[k][2 * j + 1], e5m2_pair_hi(kd[i][j]), a);
+          }
+        }
+        r[k] = a;
+      }
+      row_reduce_heads<G>(r);
+      const bool live = (4 * i + row) < tok_lim;
+      sc[i] = live ? r[0] * p.scale_log2 : -__builtin_inff();
+    }
+    // online softmax for this row's own head, threshold rescale
+    float bmax = sc[0];
+#pragma unroll
+    for (int i = 1; i < NL; ++i) bmax = fmaxf(bmax, sc[i]);
+    const bool need = bmax > m_own + TAU;
+    if (__any(need)) {
+      const float mn = need ? bmax : m_own;
+      const float alpha = need ? fast_exp2(m_own - mn) : 1.f;
+      l_own *= alpha;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ah = bcast_head<G>(alpha, h);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= ah;
+      }
+      m_own = mn;
+    }
+    float pr[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) pr[i] = (4 * i + row) < tok_lim ? fast_exp2(sc[i] - m_own) : 0.f;
+    if (tok_lim < 16) {  // tail or skipped block: unwritten slots may hold anything (NaN)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const bool live = (4 * i + row) < tok_lim;
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) vd[i][j] = live ? vd[i][j] : 0u;
+      }
+    }
+    if constexpr (KV == KV_E5M2) {
+#pragma unroll
+      for (int i = 0; i < NL; i += 2) {
+        const uint32_t pp = pack_f16x2_rne(pr[i], pr[i + 1]);
+        l_own += f16lo(pp) + f16hi(pp);
+        uint32_t vp[EPL];
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) {
+          vp[4 * j + 0] = e5m2_cross_pair<0>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 1] = e5m2_cross_pair<1>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 2] = e5m2_cross_pair<2>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 3] = e5m2_cross_pair<3>(vd[i][j], vd[i + 1][j]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const uint32_t ph = bcast_head_u32<G>(pp, h);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = dot2_f16(ph, vp[e], acc[h][e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        l_own += pr[i];
+        float vf[EPL];
+        if constexpr (KV == KV_F32) {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) vf[e] = as_f32(vd[i][e]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NDW; ++j) {
+            vf[2 * j] = bf16lo(vd[i][j]);
+            vf[2 * j + 1] = bf16hi(vd[i][j]);
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ph = bcast_head<G>(pr[i], h);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+        }
+      }
+    }
+  };
+
+  // ---- stream the partition's tiles, one tile of prefetch per wave ----------------------
+  // The steady-state loop issues the next tile's loads unconditionally, so the compiler's
+  // wait counters see a fixed number of loads in flight and wait only for the tile being
+  // consumed; the last one or two tiles are peeled off.
+  {
+    const int ntiles = b_first < b_end ? (b_end - b_first + W - 1) / W : 0;
+    if (ntiles > 0) {
+      uint32_t ka[NL][NDW], va[NL][NDW], kb[NL][NDW], vb[NL][NDW];
+      int b = b_first;
+      int oka = load_tile(b, ka, va), okb;
+      int i = 0;
+      for (; i + 2 < ntiles; i += 2) {
+        okb = load_tile(b + W, kb, vb);
+        compute_tile(b, oka, ka, va);
+        oka = load_tile(b + 2 * W, ka, va);
+        compute_tile(b + W, okb, kb, vb);
+        b += 2 * W;
+      }
+      if (i + 1 < ntiles) {
+        okb = load_tile(b + W, kb, vb);
+        compute_tile(b, oka, ka, va);
+        compute_tile(b + W, okb, kb, vb);
+      } else {
+        compute_tile(b, oka, ka, va);
+      }
+    }
+  }
+
+  // ---- merge the four rows of the wave ----------------------------------------------------
+  float mw = fmaxf(m_own, __shfl_xor(m_own, 16));
+  mw = fmaxf(mw, __shfl_xor(mw, 32));
+  const float ar = (m_own == -__builtin_inff()) ? 0.f : fast_exp2(m_own - mw);
+  float lw = l_own * ar;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float ah = bcast_head<G>(ar, h);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float v = acc[h][e] * ah;
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      acc[h][e] = v;
+    }
+  }
+
+  const bool final_out = nparts <= 1;
+  const size_t out_row = ((size_t)qrow * hq + (size_t)g * G) * D;  // first head of the group
+  const size_t ws_row = ((size_t)s * hq + (size_t)g * G) * p.max_parts;
+
+  auto emit = [&](int h, int d, float num, float den, float mval) {
+    const float o = den > 0.f ? num / den : 0.f;
+    if (final_out) {
+      if constexpr (KV == KV_F32) {
+        reinterpret_cast<float*>(p.out)[out_row + (size_t)h * D + d] = o;
+      } else {
+        reinterpret_cast<uint16_t*>(p.out)[out_row + (size_t)h * D + d] = (uint16_t)f32_to_bf16_rne(o);
+      }
+    } else {
+      const size_t j = ws_row + (size_t)h * p.max_parts + part;
+      p.ws_o[j * D + d] = o;
+      if (d == 0) {
+        p.ws_m[j] = mval;
+        p.ws_l[j] = den;
+      }
+    }
+  };
+
+  if constexpr (W == 1) {
+    if (row == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float lh = bcast_head<G>(lw, h);
+        const float mh = bcast_head<G>(mw, h);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) emit(h, col * EPL + e, acc[h][e], lh, mh);
+      }
+    }
+  } else {
+    __shared__ float sm_acc[W][G][D];
+    __shared__ float sm_m[W][G];
+    __shared__ float sm_l[W][G];
+    if (row == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sm_acc[wave][h][col * EPL + e] = acc[h][e];
+      if ((col & (16 / G - 1)) == 0) {
+        sm_m[wave][col / (16 / G)] = mw;
+        sm_l[wave][col / (16 / G)] = lw;
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
+      const int h = idx / D, d = idx % D;
+      float mx = sm_m[0][h];
+#pragma unroll
+      for (int w = 1; w < W; ++w) mx = fmaxf(mx, sm_m[w][h]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float mwv = sm_m[w][h];
+        const float a = (mwv == -__builtin_inff()) ? 0.f : fast_exp2(mwv - mx);
+        num = fmaf(a, sm_acc[w][h][d], num);
+        den = fmaf(a, sm_l[w][h], den);
+      }
+      emit(h, d, num, den, mx);
+    }
+  }
+}
+
+// Merge the partitions of every (sequence, query head) that was split.
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeParams p) {
+  constexpr int PER = D / 64;
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int hq = gridDim.x;
+  int qrow = s;
+  if (p.cu_q != nullptr) {
+    const int a = load_invariant(p.cu_q + s), b = load_invariant(p.cu_q + s + 1);
+    if (b - a != 1) return;
+    qrow = a;
+  }
+  int L = load_invariant(p.context_lens + s);
+  L = L < 0 ? 0 : L;
+  L = L > p.max_context_len ? p.max_context_len : L;
+  L = L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
+  const int nparts = (L + p.partition_tokens - 1) / p.partition_tokens;
+  if (nparts <= 1) return;
+  const size_t base = ((size_t)s * hq + h) * p.max_parts;
+  float mx = -__builtin_inff();
+  for (int j = 0; j < nparts; ++j) mx = fmaxf(mx, p.ws_m[base + j]);
+  float den = 0.f;
+  float num[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  for (int j = 0; j < nparts; ++j) {
+    const float mj = p.ws_m[base + j];
+    const float w = (mj == -__builtin_inff()) ? 0.f : fast_exp2(mj - mx) * p.ws_l[base + j];
+    den += w;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) num[e] = fmaf(w, p.ws_o[(base + j) * D + threadIdx.x + 64 * e], num[e]);
+  }
+  const size_t orow = ((size_t)qrow * hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const float o = den > 0.f ? num[e] / den : 0.f;
+    if constexpr (OUT_BF16)
+      reinterpret_cast<uint16_t*>(p.out)[orow + threadIdx.x + 64 * e] = (uint16_t)f32_to_bf16_rne(o);
+    else
+      reinterpret_cast<float*>(p.out)[orow + threadIdx.x + 64 * e] = o;
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <int KV, int D, int G>
+static hipError_t launch_parts_kv_d_g(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+  constexpr int W = 4;
+  dim3 grid(p.max_parts, p.num_kv_heads, num_seqs);
+  hipLaunchKernelGGL((decode_partition_kernel<KV, D, G, W>), grid, dim3(64 * W), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int KV, int D>
+static hipError_t launch_parts_kv_d(const DecodeParams& p, int gqa, int num_seqs, hipStream_t stream) {
+  switch (gqa) {
+    case 1: return launch_parts_kv_d_g<KV, D, 1>(p, num_seqs, stream);
+    case 2: return launch_parts_kv_d_g<KV, D, 2>(p, num_seqs, stream);
+    case 4: return launch_parts_kv_d_g<KV, D, 4>(p, num_seqs, stream);
+    case 8: return launch_parts_kv_d_g<KV, D, 8>(p, num_seqs, stream);
+    case 16: return launch_parts_kv_d_g<KV, D, 16>(p, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
+                                    hipStream_t stream) {
+  if (head_dim == 128) {
+    if (kv_kind == KV_F32) return launch_parts_kv_d<KV_F32, 128>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_BF16) return launch_parts_kv_d<KV_BF16, 128>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_E5M2) return launch_parts_kv_d<KV_E5M2, 128>(p, gqa, num_seqs, stream);
+  } else if (head_dim == 64) {
+    if (kv_kind == KV_F32) return launch_parts_kv_d<KV_F32, 64>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_BF16) return launch_parts_kv_d<KV_BF16, 64>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_E5M2) return launch_parts_kv_d<KV_E5M2, 64>(p, gqa, num_seqs, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
+                                hipStream_t stream) {
+  if (p.max_parts <= 1) return hipSuccess;
+  dim3 grid(num_q_heads, num_seqs);
+  if (head_dim == 128) {
+    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<128, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((decode_reduce_kernel<128, false>), grid, dim3(64), 0, stream, p);
+  } else if (head_dim == 64) {
+    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<64, true>), grid, dim3(64), 0, stream, p);
+    else hipLaunchKernelGGL((decode_reduce_kernel<64, false>), grid, dim3(64), 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

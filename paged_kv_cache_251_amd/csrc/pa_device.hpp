@@ -1,0 +1,220 @@
+// Device helpers shared by the libpagedattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_launch.hpp"
+
+namespace pa {
+
+template <int KV>
+struct KvBytes;
+template <>
+struct KvBytes<KV_F32> { static constexpr int value = 4; };
+template <>
+struct KvBytes<KV_BF16> { static constexpr int value = 2; };
+template <>
+struct KvBytes<KV_E5M2> { static constexpr int value = 1; };
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+__device__ __forceinline__ uint32_t as_u32(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// ---------------------------------------------------------------------------
+// DPP lane exchange inside one 16-lane row.  Pairings used by the reductions:
+//   bit 3: row_mirror       lane i <- 15 - i
+//   bit 2: row_half_mirror  lane i <- (i & 8) | (7 - (i & 7))
+//   bit 1: quad_perm 2301   lane i <- i ^ 2
+//   bit 0: quad_perm 1032   lane i <- i ^ 1
+// Each flips the named bit of the lane index (and possibly lower bits only).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int DPP_ROW_BCAST0 = 0x150;  // row_newbcast:n = 0x150 + n (lane n of each row)
+
+template <int BIT>
+struct PairCtrl;
+template <>
+struct PairCtrl<3> { static constexpr int value = DPP_ROW_MIRROR; };
+template <>
+struct PairCtrl<2> { static constexpr int value = DPP_ROW_HALF_MIRROR; };
+template <>
+struct PairCtrl<1> { static constexpr int value = DPP_QUAD_XOR2; };
+template <>
+struct PairCtrl<0> { static constexpr int value = DPP_QUAD_XOR1; };
+
+// Host-visible twin of the pairings above, on a lane index within a row.
+__host__ __device__ constexpr int pair_lane(int bit, int x) {
+  return bit == 3 ? 15 - x : bit == 2 ? ((x & 8) | (7 - (x & 7))) : bit == 1 ? (x ^ 2) : (x ^ 1);
+}
+
+// Head held in register slot k of lane `col` (0..15) before the head-distributing
+// reduction over G heads (see row_reduce_heads).
+template <int G>
+__device__ __forceinline__ int head_of_slot(int col, int k) {
+  constexpr int S = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
+  int y = col;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    if (k & (G >> (s + 1))) y = pair_lane(3 - s, y);
+  return S == 0 ? 0 : (y >> (4 - S));
+}
+
+// Sum G per-lane partial dot products over the 16 lanes of a row while spreading
+// the heads over the lanes: on entry slot k of lane col holds the partial of head
+// head_of_slot<G>(col, k); on exit r[0] holds the full sum for head col >> (4 - S)
+// (S = log2 G), identical on the 16/G lanes that share that head.  Each step keeps
+// the first half of the live slots and adds the partner lane's second half, so the
+// row costs log2(16) steps with G-1 + (4-S) DPP adds instead of 4G.
+template <int G>
+__device__ __forceinline__ void row_reduce_heads(float (&r)[G]) {
+  int n = G;
+#define PA_STEP(BIT)                                                             \
+  {                                                                              \
+    if (n > 1) {                                                                 \
+      const int half = n >> 1;                                                   \
+      _Pragma("unroll") for (int k = 0; k < G / 2; ++k) if (k < half) r[k] +=    \
+          dpp_f32<PairCtrl<BIT>::value>(r[half + k]);                            \
+      n = half;                                                                  \
+    } else {                                                                     \
+      r[0] += dpp_f32<PairCtrl<BIT>::value>(r[0]);                               \
+    }                                                                            \
+  }
+  PA_STEP(3) PA_STEP(2) PA_STEP(1) PA_STEP(0)
+#undef PA_STEP
+}
+
+// Lane index (within a row) that holds head h's reduced value.
+template <int G>
+__device__ __forceinline__ constexpr int head_lane(int h) {
+  return h * (16 / G);
+}
+
+// Broadcast lane LANE of each 16-lane row to the whole row.
+template <int LANE>
+__device__ __forceinline__ float row_bcast(float v) {
+  return dpp_f32<DPP_ROW_BCAST0 + LANE>(v);
+}
+template <int LANE>
+__device__ __forceinline__ uint32_t row_bcast_u32(uint32_t v) {
+  return dpp_u32<DPP_ROW_BCAST0 + LANE>(v);
+}
+
+// ---------------------------------------------------------------------------
+// element conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return as_f32(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return as_f32(w & 0xFFFF0000u); }
+
+// binary32 -> bfloat16, round to nearest even; NaN -> quiet NaN with sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = as_u32(f);
+  uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? (((u >> 16) & 0x8000u) | 0x7FC0u) : r;
+}
+
+// bfloat16 (16-bit pattern) -> E5M2 code, round to nearest even, no saturation:
+// a magnitude that rounds past 57344 becomes inf; NaN -> sign | 0x7F.
+__device__ __forceinline__ uint32_t bf16_to_e5m2(uint32_t b) {
+  const uint32_t sign = (b >> 8) & 0x80u;
+  const uint32_t a = b & 0x7FFFu;
+  // |x| >= 2^-14: move the exponent from bias 127 to bias 15, drop 5 mantissa bits
+  const uint32_t x = a - (112u << 7);
+  uint32_t qn = x >> 5;
+  const uint32_t rn = x & 31u;
+  qn += (rn > 16u) | ((rn == 16u) & (qn & 1u));
+  qn = qn > 0x7Cu ? 0x7Cu : qn;
+  // |x| < 2^-14: code = value / 2^-16 rounded to nearest even (0..4)
+  const uint32_t e = a >> 7;
+  const uint32_t mant = (a & 0x7Fu) | 0x80u;
+  const uint32_t sh = 118u - e;  // >= 6 here
+  const uint32_t shc = sh > 9u ? 9u : sh;
+  uint32_t qs = mant >> shc;
+  const uint32_t rs = mant & ((1u << shc) - 1u);
+  const uint32_t half = 1u << (shc - 1u);
+  qs += (rs > half) | ((rs == half) & (qs & 1u));
+  qs = (sh > 9u || e == 0u) ? 0u : qs;
+  uint32_t code = a >= (113u << 7) ? qn : qs;
+  code = a > 0x7F80u ? 0x7Fu : code;
+  return sign | code;
+}
+
+// Four E5M2 codes (bytes of w) -> two f16x2 words; exact (an E5M2 code is the upper
+// byte of the f16 with the same value).
+__device__ __forceinline__ uint32_t e5m2_pair_lo(uint32_t w) {
+  return __builtin_amdgcn_perm(0u, w, 0x010C000Cu);
+}
+__device__ __forceinline__ uint32_t e5m2_pair_hi(uint32_t w) {
+  return __builtin_amdgcn_perm(0u, w, 0x030C020Cu);
+}
+
+// (byte j of a, byte j of b) as an f16x2 word, low half from a.
+template <int J>
+__device__ __forceinline__ uint32_t e5m2_cross_pair(uint32_t a, uint32_t b) {
+  // v_perm: bytes 0-3 select from the second source (a), 4-7 from the first (b)
+  constexpr uint32_t sel = 0x0Cu | ((uint32_t)J << 8) | (0x0Cu << 16) | ((uint32_t)(4 + J) << 24);
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// Two binary32 -> f16x2, each rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2_rne(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
+
+// ---------------------------------------------------------------------------
+// vector loads of N dwords (N = 1, 2, 4, 8)
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void load_dw(uint32_t (&d)[N], const void* p) {
+  if constexpr (N == 1) {
+    d[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (N == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    d[0] = v.x; d[1] = v.y;
+  } else if constexpr (N == 4) {
+    uint4 v = *reinterpret_cast<const uint4*>(p);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+  } else {
+    uint4 v = reinterpret_cast<const uint4*>(p)[0];
+    uint4 w = reinterpret_cast<const uint4*>(p)[1];
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    d[4] = w.x; d[5] = w.y; d[6] = w.z; d[7] = w.w;
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Read a value that no kernel of this launch writes (block tables, lengths) through the
+// constant address space, so that a wave-uniform address becomes a scalar load.
+template <typename T>
+__device__ __forceinline__ T load_invariant(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      reinterpret_cast<const __attribute__((address_space(4))) char*>(reinterpret_cast<uintptr_t>(p)));
+}
+
+}  // namespace pa

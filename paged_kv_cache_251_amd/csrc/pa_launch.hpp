@@ -1,0 +1,50 @@
+// Internal launch interface between the host C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Element type of a pool (values match pa_dtype_t).
+enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_E5M2 = 2 };
+
+struct DecodeParams {
+  void* out;
+  float* ws_o;  // [rows][hq][max_parts][D]
+  float* ws_m;  // [rows][hq][max_parts]
+  float* ws_l;  // [rows][hq][max_parts]
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_q;  // null: decode batch (query row s); else packed varlen rows
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t max_context_len;
+  int32_t partition_tokens;  // 0: one pass per context
+  int32_t max_parts;         // grid.x: partitions of the longest context (1 if unsplit)
+  float scale_log2;          // scale * log2(e)
+};
+
+// Partition pass: a sequence with one partition gets its output row; a split one gets
+// (o/l, m, l) per partition in the workspace.
+hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
+                                    hipStream_t stream);
+// Merge pass over the split sequences (no-op when p.max_parts <= 1).
+hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
+                                hipStream_t stream);
+
+hipError_t launch_slot_mapping(int32_t* slots, const int32_t* cu, const int32_t* end_pos,
+                               const int32_t* tables, int32_t max_blocks, int32_t num_seqs,
+                               int32_t num_tokens, int32_t block_size, int32_t num_blocks,
+                               hipStream_t stream);
+
+hipError_t launch_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                              const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, int src_kind,
+                              int cache_kind, hipStream_t stream);
+
+}  // namespace pa
