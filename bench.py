@@ -2,8 +2,12 @@
 """Paged decode attention benchmark on one MI355X.
 
 One step = the whole decode path for one batch: slot mapping of each sequence's
-newest token, the cache write of its K/V row, the paged attention partition pass
-and (when the context is split) the reduce pass.  Several independently seeded
+newest token, the cache write of its K/V row (cast to E5M2 for an fp8 cache),
+the paged attention partition pass and, when contexts are split, the reduce
+pass.  The timed step runs these as one fused launch
+(paged_attention_decode_append; plus the reduce kernel when split); the same
+step as three separate calls (slot mapping, kv_cache_write, decode) is timed
+too and reported as ``unfused``.  Several independently seeded
 batches of the same shape are resident and steps rotate over them, so a timed
 step never re-reads a pool that an earlier step left in the 256 MB Infinity
 Cache.  Inputs are synthetic (seeded N(0,1) values with the workload's shapes).
@@ -39,8 +43,25 @@ def parse():
     ap.add_argument("--partition", type=int, default=None, help="partition tokens (default: workload's, else auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", type=str, default=None, help="JSON file with measured HBM bytes per launch")
+    ap.add_argument("--traffic", type=str, default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
+                    help="measured HBM bytes per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES between two device buffers 3 times (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(nbytes: int) -> None:
+    """A plain device copy of known size: under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE
+    per dispatch against nbytes give the scale of the counters."""
+    import torch
+
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "dispatches": 3}), flush=True)
 
 
 class Batch:
@@ -92,11 +113,17 @@ class Batch:
                            d, bs, nb, ml, w.scale, qd, kd, partition, P(self.ws), self.ws.numel())
         self.args_reduce = (P(self.out), P(self.lens), mb, n, hkv, g, d, bs, ml, qd, kd, partition, P(self.ws),
                             self.ws.numel())
+        self.args_append = (P(self.out), P(self.q), P(self.knew), P(self.vnew), P(self.pk), P(self.pv), P(self.tables),
+                            mb, P(self.lens), n, hkv, g, d, bs, nb, ml, w.scale, qd, kd, partition,
+                            pa.binding.PA_APPEND_SKIP_REDUCE, P(self.ws), self.ws.numel())
         self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * d * 2 * KV_BYTES[w.kv_dtype]
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path needs no second GPU)",
               file=sys.stderr)
@@ -135,42 +162,56 @@ def main():
             raise RuntimeError(f"{fn}: {lib.pa_last_error().decode()}")
 
     def step(b, ev=None):
-        check(lib.paged_kv_slot_mapping(*b.args_slot, sh), "slot mapping")
-        check(lib.kv_cache_write(*b.args_write, sh), "cache write")
+        """Fused step: append + attend in one launch (+ the reduce kernel for split contexts)."""
         if ev is not None:
             ev[0].record(stream)
-        check(lib.paged_attention_decode_partitions(*b.args_parts, sh), "decode partitions")
+        check(lib.paged_attention_decode_append(*b.args_append, sh), "decode append")
         if ev is not None:
             ev[1].record(stream)
         if b.split:
             check(lib.paged_attention_decode_reduce(*b.args_reduce, sh), "decode reduce")
 
-    for i in range(args.warmup):
-        step(batches[i % reps])
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        step(batches[i % reps], evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    def step_unfused(b):
+        check(lib.paged_kv_slot_mapping(*b.args_slot, sh), "slot mapping")
+        check(lib.kv_cache_write(*b.args_write, sh), "cache write")
+        check(lib.paged_attention_decode_partitions(*b.args_parts, sh), "decode partitions")
+        if b.split:
+            check(lib.paged_attention_decode_reduce(*b.args_reduce, sh), "decode reduce")
+
+    def timed(fn, with_events):
+        for i in range(args.warmup):
+            fn(batches[i % reps])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] if with_events else None
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for i in range(args.steps):
+            if with_events:
+                fn(batches[i % reps], evs[i])
+            else:
+                fn(batches[i % reps])
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        kern = [a.elapsed_time(b) for a, b in evs] if with_events else None
+        return start.elapsed_time(stop) / args.steps, wall, kern
+
+    # unfused path first (it also warms the clocks), then the roofline loop (a HIP event
+    # pair around the partition kernel of every step), then the reported steps, back to
+    # back with no events between launches
+    ms_unfused, _, _ = timed(step_unfused, False)
+    _, _, kern_ms = timed(step, True)
+    ms_step, wall, _ = timed(step, False)
     kern_avg = float(np.mean(kern_ms))
     step_bytes = float(np.mean([batches[i % reps].kv_bytes for i in range(args.steps)]))
     seqs = w0.num_seqs
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     kern_gbs = step_bytes / (kern_avg * 1e-3) / 1e9
 
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get(CONFIG_NAMES[args.config])
+    traffic = measured_traffic(args.traffic, CONFIG_NAMES[args.config])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -199,15 +240,19 @@ def main():
             "context_lens": f"{int(w0.context_lens.min())}..{int(w0.context_lens.max())}",
             "partition_tokens": batches[0].resolved,
             "resident_batches": reps,
-            "step": "slot mapping + cache write (newest token) + decode partitions" +
-                    (" + reduce" if batches[0].split else ""),
+            "step": "one launch: slot mapping + cache write of the newest token + decode attention" +
+                    (" (split-KV partitions) + the separate reduce kernel" if batches[0].split else ""),
         },
         "seq_steps_per_s": round(seqs / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(step_bytes),
+        "unfused": {"ms_per_step": round(ms_unfused, 5),
+                    "GB_per_s": round(step_bytes / (ms_unfused * 1e-3) / 1e9, 2),
+                    "calls": "paged_kv_slot_mapping + kv_cache_write + decode partitions" +
+                             (" + separate reduce kernel" if batches[0].split else "")},
         "wall_s": round(wall, 4),
         "roofline": {
-            "kernel": "decode_partition_kernel",
+            "kernel": "decode_partition_kernel (append mode)",
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -220,6 +265,33 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the kernel sources: measured traffic only counts for the sources it was
+    measured on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_cache_251_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path, workload):
+    """HBM bytes per launch of the partition kernel for this workload, from the committed
+    rocprofv3 counter summary, or None when it is missing or was taken on other sources."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, budget_s):
@@ -236,8 +308,8 @@ def cpu_baseline(w, budget_s):
     done_seqs, done_bytes, t_used = 0, 0, 0.0
     with threadpool_limits(limits=1):
         s0 = 0
-        while t_used < budget_s and s0 < w.num_seqs:
-            sel = list(range(s0, min(s0 + 8, w.num_seqs)))
+        while t_used < budget_s:
+            sel = [(s0 + i) % w.num_seqs for i in range(8)]
             # history of these sequences (not timed: it is the state the step starts from)
             pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
                                  POISON_BITS[w.kv_dtype])
@@ -264,8 +336,8 @@ def cpu_baseline(w, budget_s):
         "seq_steps_per_s": round(done_seqs / t_used, 3),
         "cores": 1,
         "kind": "oracle",
-        "sample": f"first {done_seqs} of {w.num_seqs} sequences of the timed workload, one decode step each "
-                  f"(slot mapping, cache write of the newest token, float64 attention), {t_used:.1f} s",
+        "sample": f"{done_seqs} sequence-steps cycling over the {w.num_seqs} sequences of the timed workload "
+                  f"(slot mapping, cache write of the newest token, float64 attention each), {t_used:.1f} s",
     }
 
 

@@ -133,10 +133,11 @@ pa_status_t kv_cache_write(const void* key, const void* value, void* key_cache,
  * (0 when no sequence is split).  `partition_size` as in paged_attention_decode
  * (-1 resolves the same way the attention call will).
  *
- * Workspace layout (float32), with P = partitions per sequence and R = num_seqs:
- *   o  [R][num_q_heads][P][head_dim]   partition outputs, already divided by l
- *   m  [R][num_q_heads][P]             partition max of scale*log2(e)*q.k
- *   l  [R][num_q_heads][P]             partition sum of 2^(score - m)
+ * Workspace layout, with P = partitions of the longest context and R = num_seqs, each
+ * region starting on a 256-byte boundary (scratch: nothing carries over between calls):
+ *   o  float [R][num_q_heads][P][head_dim]   partition outputs, already divided by l
+ *   m  float [R][num_q_heads][P]             partition max of scale*log2(e)*q.k
+ *   l  float [R][num_q_heads][P]             partition sum of 2^(score - m)
  */
 size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                       int32_t gqa_group, int32_t head_dim,
@@ -211,6 +212,35 @@ pa_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens
                                           int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
                                           int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                           pa_dtype_t q_dtype, pa_dtype_t kv_dtype, int32_t partition_size,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_decode_append -- one whole decode step in one pass: the slot mapping
+ * and cache write of every sequence's newest token ("kernel 1") fused into the decode
+ * attention ("kernel 2").  [CI BlockedKeyValueCache; CI KVCache Quant; CI PagedAttention]
+ *
+ * The newest token of sequence s sits at position L-1 (L = context_lens[s], which counts
+ * it).  Its rows key[s], value[s] ([num_kv_heads][head_dim], q_dtype, dense, 16-byte
+ * aligned) are stored at slot block_tables[s][(L-1)/B]*B + (L-1)%B of the pools (cast to
+ * E5M2 when kv_dtype is FP8_E5M2, exactly as kv_cache_write casts), and the attention is
+ * paged_attention_decode over all L tokens.  The result is bit-identical to
+ * paged_kv_slot_mapping + kv_cache_write + paged_attention_decode with the same
+ * partition size.  A sequence with L = 0 appends nothing.  A slot whose table entry is
+ * outside [0, num_blocks) is not written.
+ *
+ * flags: PA_APPEND_SKIP_REDUCE -- run only the streaming pass; the caller then runs
+ *        paged_attention_decode_reduce (same arguments) when a sequence is split.
+ *        Without it the reduce kernel is launched after the streaming pass.
+ */
+#define PA_APPEND_SKIP_REDUCE 1
+
+pa_status_t paged_attention_decode_append(void* out, const void* query, const void* key, const void* value,
+                                          void* key_cache, void* value_cache, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                          int32_t max_context_len, float scale, pa_dtype_t q_dtype,
+                                          pa_dtype_t kv_dtype, int32_t partition_size, int32_t flags,
                                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     kv_cache_write,
     lib,
     paged_attention_decode,
+    paged_attention_decode_append,
     slot_mapping,
     workspace_size,
 )

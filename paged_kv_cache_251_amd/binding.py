@@ -38,7 +38,11 @@ SIGNATURES = {
                                                          _i32, _vp, _sz, _vp]),
     "paged_attention_decode_reduce": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                      ctypes.c_int, ctypes.c_int, _i32, _vp, _sz, _vp]),
+    "paged_attention_decode_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _i32,
+                                                     _i32, _vp, _sz, _vp]),
 }
+PA_APPEND_SKIP_REDUCE = 1
 
 
 class PagedAttnError(RuntimeError):
@@ -186,5 +190,39 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
         _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), n, hkv, g, d, bs, nb, max_context_len, scale, dtype_code(query),
         dtype_code(key_cache), partition_size, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream()))
+    return out
+
+
+def paged_attention_decode_append(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                                  key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, max_context_len: int, scale: float,
+                                  partition_size: int = -1, out: Optional[torch.Tensor] = None,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Write each sequence's newest K/V row [N, Hkv, D] at position L-1 and attend over all L
+    tokens, in one pass (``paged_attention_decode_append``; split contexts are then merged
+    by the reduce kernel)."""
+    _dev(query, key, value, key_cache, value_cache, block_tables, context_lens)
+    _int32(block_tables, context_lens)
+    n, hq, d = query.shape
+    nb, hkv, bs, _ = key_cache.shape
+    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    _expect(key_cache.shape[3] == d and hq % hkv == 0, "query and pools disagree on D / heads")
+    _expect(key.shape == (n, hkv, d) and value.shape == key.shape, "key/value rows must be [N, Hkv, D]")
+    _expect(key.dtype == query.dtype and value.dtype == query.dtype, "key/value rows take the query dtype")
+    _expect(block_tables.dim() == 2 and block_tables.shape[0] == n and context_lens.shape == (n,),
+            "block_tables [N, max_blocks], context_lens [N]")
+    g = hq // hkv
+    if out is None:
+        out = torch.empty_like(query)
+    _dev(out)
+    _expect(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    need = workspace_size(n, hkv, g, d, max_context_len, partition_size)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = alloc_workspace(need, query.device)
+    _check("paged_attention_decode_append", lib().paged_attention_decode_append(
+        _ptr(out), _ptr(query), _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), n, hkv, g, d, bs, nb, max_context_len, scale, dtype_code(query),
+        dtype_code(key_cache), partition_size, 0, _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream()))
     return out

@@ -41,6 +41,10 @@ int kv_kind(pa_dtype_t t) { return t == PA_F32 ? pa::KV_F32 : t == PA_BF16 ? pa:
 bool valid_dtype(int t) { return t == PA_F32 || t == PA_BF16 || t == PA_FP8_E5M2; }
 
 constexpr int64_t kMaxGridYZ = 65535;
+
+#ifndef PA_LONGEST_FIRST
+#define PA_LONGEST_FIRST 1  // dispatch the decode work-groups of long contexts first
+#endif
 constexpr size_t kWsAlign = 256;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -55,9 +59,12 @@ struct WsLayout {
   size_t o_bytes, ml_bytes, total;
 };
 
-WsLayout ws_layout(int64_t rows, int64_t hq, int64_t head_dim, int64_t parts) {
+// o [rows][hq][parts][D] f32 | m [rows][hq][parts] f32 | l [rows][hq][parts] f32,
+// each region 256-byte aligned.
+WsLayout ws_layout(int64_t rows, int64_t hkv, int64_t gqa, int64_t head_dim, int64_t parts) {
   WsLayout w{0, 0, 0};
   if (parts <= 1 || rows <= 0) return w;
+  const int64_t hq = hkv * gqa;
   w.o_bytes = round_up(static_cast<size_t>(rows * hq * parts * head_dim) * sizeof(float), kWsAlign);
   w.ml_bytes = round_up(static_cast<size_t>(rows * hq * parts) * sizeof(float), kWsAlign);
   w.total = w.o_bytes + 2 * w.ml_bytes;
@@ -65,10 +72,11 @@ WsLayout ws_layout(int64_t rows, int64_t hq, int64_t head_dim, int64_t parts) {
 }
 
 int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  // Enough (partition, KV head, sequence) work-groups to keep every CU busy several
-  // times over: 256 CUs, aim for ~2048 groups.  Partitions are multiples of 256 tokens.
+  // With at least one (KV head, sequence) context per CU (256 CUs) every context is
+  // streamed whole, longest first: no partial results, no merge.  Fewer, longer contexts
+  // are split into multiples of 256 tokens, aiming at ~2048 work-groups.
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  if (units <= 0 || units >= 2048 || max_context_len <= 256) return 0;
+  if (units <= 0 || units >= 256 || max_context_len <= 256) return 0;
   int64_t p = static_cast<int64_t>(max_context_len) * units / 2048;
   p = (p + 255) / 256 * 256;
   if (p < 256) p = 256;
@@ -213,7 +221,7 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_kv_heads, in
   const int32_t part = partition_size == -1 ? auto_partition(num_seqs, num_kv_heads, max_context_len)
                                             : partition_size;
   const int64_t parts = parts_for(max_context_len, part);
-  return ws_layout(num_seqs, static_cast<int64_t>(num_kv_heads) * gqa_group, head_dim, parts).total;
+  return ws_layout(num_seqs, num_kv_heads, gqa_group, head_dim, parts).total;
 }
 
 }  // extern "C"
@@ -243,15 +251,14 @@ pa_status_t prepare_decode(const char* fn, pa::DecodeParams& p, void* out, const
   const int32_t part = partition_size == -1 ? auto_partition(num_seqs, num_kv_heads, max_context_len)
                                             : partition_size;
   const int64_t parts = parts_for(max_context_len, part);
-  const int64_t hq = static_cast<int64_t>(num_kv_heads) * gqa_group;
-  const WsLayout ws = ws_layout(num_seqs, hq, head_dim, parts);
+  const WsLayout ws = ws_layout(num_seqs, num_kv_heads, gqa_group, head_dim, parts);
   if (ws.total > 0) {
     if (workspace == nullptr) return fail(PA_ERR_INVALID_ARGUMENT, "%s: workspace is null, need %zu bytes", fn, ws.total);
     if (workspace_bytes < ws.total)
       return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu bytes, need %zu", fn, workspace_bytes, ws.total);
     if (!aligned(workspace, kWsAlign)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: workspace must be 256-byte aligned", fn);
   }
-  if (parts > (int64_t(1) << 31) - 1) return fail(PA_ERR_UNSUPPORTED, "%s: too many partitions", fn);
+  if (parts > kMaxGridYZ) return fail(PA_ERR_UNSUPPORTED, "%s: %lld partitions > 65535", fn, (long long)parts);
   p = pa::DecodeParams{};
   p.out = out;
   p.ws_o = ws.total ? static_cast<float*>(workspace) : nullptr;
@@ -270,6 +277,8 @@ pa_status_t prepare_decode(const char* fn, pa::DecodeParams& p, void* out, const
   p.partition_tokens = parts > 1 ? part : 0;
   p.max_parts = static_cast<int32_t>(parts);
   p.scale_log2 = scale * 1.4426950408889634f;
+  // longest-first only pays when whole contexts are the work units (see decode.hip)
+  p.longest_first = PA_LONGEST_FIRST && parts <= 1 && num_seqs <= 1024;
   return PA_OK;
 }
 
@@ -329,6 +338,35 @@ pa_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens
   return device_status(pa::launch_decode_reduce(p, q_dtype == PA_BF16, head_dim, num_kv_heads * gqa_group, num_seqs,
                                                 stream),
                        fn);
+}
+
+pa_status_t paged_attention_decode_append(void* out, const void* query, const void* key, const void* value,
+                                          void* key_cache, void* value_cache, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                                          int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
+                                          pa_dtype_t q_dtype, pa_dtype_t kv_dtype, int32_t partition_size,
+                                          int32_t flags, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream) {
+  const char* fn = "paged_attention_decode_append";
+  if (flags & ~PA_APPEND_SKIP_REDUCE) return fail(PA_ERR_INVALID_ARGUMENT, "%s: unknown flags 0x%x", fn, flags);
+  pa::DecodeParams p;
+  pa_status_t st = prepare_decode(fn, p, out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                                  context_lens, num_seqs, num_kv_heads, gqa_group, head_dim, block_size, num_blocks,
+                                  max_context_len, scale, q_dtype, kv_dtype, partition_size, workspace,
+                                  workspace_bytes, true);
+  if (st != PA_OK || num_seqs == 0) return st == PA_OK ? ok() : st;
+  if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "%s: null key/value row pointer", fn);
+  if (!aligned(key, 16) || !aligned(value, 16))
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: key/value rows must be 16-byte aligned", fn);
+  p.key_new = key;
+  p.value_new = value;
+  p.key_cache_w = key_cache;
+  p.value_cache_w = value_cache;
+  hipError_t e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
+  if (e == hipSuccess && !(flags & PA_APPEND_SKIP_REDUCE))
+    e = pa::launch_decode_reduce(p, q_dtype == PA_BF16, head_dim, num_kv_heads * gqa_group, num_seqs, stream);
+  return device_status(e, fn);
 }
 
 }  // extern "C"

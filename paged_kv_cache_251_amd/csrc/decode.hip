@@ -30,6 +30,11 @@
 namespace pa {
 
 constexpr float TAU = 8.0f;
+constexpr int kMaxRankedSeqs = 1024;  // longest-first ordering is used up to this batch size
+
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS true  // KV tiles are streamed once per step
+#endif
 
 template <int G>
 __device__ __forceinline__ float bcast_head(float v, int h) {
@@ -74,8 +79,28 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane >> 4, col = lane & 15;
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int g = blockIdx.x, part = blockIdx.y;
   const int hq = p.num_kv_heads * G;
+  int s = blockIdx.z;
+  if (p.longest_first) {
+    // rank of sequence t = #{t' : L[t'] > L[t] or (L[t'] == L[t] and t' < t)}; invert it
+    __shared__ int sm_len[kMaxRankedSeqs];
+    __shared__ int sm_order[kMaxRankedSeqs];
+    const int n = gridDim.z;
+    for (int t = threadIdx.x; t < n; t += 64 * W) sm_len[t] = load_invariant(p.context_lens + t);
+    __syncthreads();
+    for (int t = threadIdx.x; t < n; t += 64 * W) {
+      const int lt = sm_len[t];
+      int r = 0;
+      for (int u = 0; u < n; ++u) {
+        const int lu = sm_len[u];
+        r += (lu > lt) | ((lu == lt) & (u < t));
+      }
+      sm_order[r] = t;
+    }
+    __syncthreads();
+    s = sm_order[blockIdx.z];
+  }
 
   int qrow = s;
   if (p.cu_q != nullptr) {  // packed varlen batch: this kernel serves the 1-token rows
@@ -96,7 +121,9 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   if (part > 0 && t0 >= L) return;
 
   // ---- the query group, in this lane's head order -------------------------------------
+  // (raw loads only here; they are waited for after the first tile's loads are issued)
   uint32_t qv[G][QDW];
+  uint32_t qraw[G][KV == KV_E5M2 ? QDW : 1];
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     const int h = head_of_slot<G>(col, k);
@@ -105,19 +132,74 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       load_dw<QDW>(qv[k], reinterpret_cast<const float*>(p.query) + qoff);
     } else if constexpr (KV == KV_BF16) {
       load_dw<QDW>(qv[k], reinterpret_cast<const uint16_t*>(p.query) + qoff);
-    } else {  // bf16 query against an E5M2 cache: widen to f16 pairs once
-      uint32_t raw[QDW];
-      load_dw<QDW>(raw, reinterpret_cast<const uint16_t*>(p.query) + qoff);
-#pragma unroll
-      for (int j = 0; j < QDW; ++j) qv[k][j] = pack_f16x2_rne(bf16lo(raw[j]), bf16hi(raw[j]));
+    } else {
+      load_dw<QDW>(qraw[k], reinterpret_cast<const uint16_t*>(p.query) + qoff);
     }
   }
-  // Consume the query registers here so that their load is waited for once, before the
-  // tile loop; otherwise the wait lands inside the loop and also drains the prefetch.
+  // ---- append mode: the newest token's K/V row ----------------------------------------
+  // Only the work-group whose partition holds position L-1 appends; its row r_new of tile
+  // b_new then comes from the new row instead of the cache (no read-after-write inside
+  // the launch).  Lane (row, col) keeps columns col*EPL .. col*EPL+EPL-1 in cache format.
+  const int pos_new = L - 1;
+  const bool appending = p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
+  const int b_new = appending ? pos_new / 16 : -1;
+  const int r_new = pos_new & 15;
+  uint32_t knew[NDW], vnew[NDW];
+  uint32_t kraw[KV == KV_E5M2 ? 2 * NDW : 1], vraw[KV == KV_E5M2 ? 2 * NDW : 1];
+  if (appending) {
+    const size_t roff = ((size_t)s * p.num_kv_heads + g) * D + (size_t)col * EPL;  // element offset
+    if constexpr (KV == KV_F32) {
+      load_dw<NDW>(knew, reinterpret_cast<const float*>(p.key_new) + roff);
+      load_dw<NDW>(vnew, reinterpret_cast<const float*>(p.value_new) + roff);
+    } else if constexpr (KV == KV_BF16) {
+      load_dw<NDW>(knew, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
+      load_dw<NDW>(vnew, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
+    } else {
+      load_dw<2 * NDW>(kraw, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
+      load_dw<2 * NDW>(vraw, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
+    }
+  }
+  // Once the first tile is in flight: cast the new row to the cache type (bf16 -> E5M2 is
+  // the cache write's own cast) and store it at its slot.
+  auto finish_append = [&]() {
+    if (!appending) return;
+    if constexpr (KV == KV_E5M2) {
 #pragma unroll
-  for (int k = 0; k < G; ++k)
+      for (int j = 0; j < NDW; ++j) {
+        knew[j] = bf16_to_e5m2(kraw[2 * j] & 0xFFFFu) | (bf16_to_e5m2(kraw[2 * j] >> 16) << 8) |
+                  (bf16_to_e5m2(kraw[2 * j + 1] & 0xFFFFu) << 16) | (bf16_to_e5m2(kraw[2 * j + 1] >> 16) << 24);
+        vnew[j] = bf16_to_e5m2(vraw[2 * j] & 0xFFFFu) | (bf16_to_e5m2(vraw[2 * j] >> 16) << 8) |
+                  (bf16_to_e5m2(vraw[2 * j + 1] & 0xFFFFu) << 16) | (bf16_to_e5m2(vraw[2 * j + 1] >> 16) << 24);
+      }
+    }
+    const int phys = load_invariant(p.block_tables + (size_t)s * p.max_blocks_per_seq + b_new);
+    if (wave == 0 && row == 0 && phys >= 0 && phys < p.num_blocks) {
+      const size_t dst = ((((size_t)phys * p.num_kv_heads + g) * 16 + r_new) * D + (size_t)col * EPL) * SZ;
+      uint32_t* kc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + dst);
+      uint32_t* vc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.value_cache_w) + dst);
 #pragma unroll
-    for (int j = 0; j < QDW; ++j) asm volatile("" ::"v"(qv[k][j]));
+      for (int j = 0; j < NDW; ++j) {
+        kc[j] = knew[j];
+        vc[j] = vnew[j];
+      }
+    }
+  };
+
+  // After the first tile is in flight: widen a bf16 query to f16 pairs for an E5M2 cache,
+  // and make every query register ready before the tile loop (so that the loop's own
+  // waits only count tile loads).
+  auto finish_query = [&]() {
+    if constexpr (KV == KV_E5M2) {
+#pragma unroll
+      for (int k = 0; k < G; ++k)
+#pragma unroll
+        for (int j = 0; j < QDW; ++j) qv[k][j] = pack_f16x2_rne(bf16lo(qraw[k][j]), bf16hi(qraw[k][j]));
+    }
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+#pragma unroll
+      for (int j = 0; j < QDW; ++j) asm volatile("" ::"v"(qv[k][j]));
+  };
 
   float m_own = -__builtin_inff();  // running max (log2 domain) of this row's own head
   float l_own = 0.f;                // running sum of 2^(S - m_own) over this row's tokens
@@ -141,9 +223,9 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
     phys = ok ? phys : 0;
     const size_t off = (((size_t)phys * p.num_kv_heads + g) * tile_elems) * SZ + lane_off;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) load_dw<NDW>(kd[i], kbase + off + (size_t)i * 4 * D * SZ);
+    for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(kd[i], kbase + off + (size_t)i * 4 * D * SZ);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) load_dw<NDW>(vd[i], vbase + off + (size_t)i * 4 * D * SZ);
+    for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(vd[i], vbase + off + (size_t)i * 4 * D * SZ);
     __builtin_amdgcn_sched_barrier(0);  // issue the tile before any math that follows
     return ok;
   };
@@ -151,6 +233,17 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   auto compute_tile = [&](int b, bool ok, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW]) {
     // valid tokens of this tile: [b*16, min(b*16+16, t1)), all of them if the block is valid
     const int tok_lim = ok ? min(16, t1 - b * 16) : 0;
+    if (b == b_new) {  // the appended token: use its row, not the (not yet written) slot
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const bool mine = (4 * i + row) == r_new;
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) {
+          kd[i][j] = mine ? knew[j] : kd[i][j];
+          vd[i][j] = mine ? vnew[j] : vd[i][j];
+        }
+      }
+    }
     float sc[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
@@ -260,6 +353,8 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       uint32_t ka[NL][NDW], va[NL][NDW], kb[NL][NDW], vb[NL][NDW];
       int b = b_first;
       int oka = load_tile(b, ka, va), okb;
+      finish_query();
+      finish_append();
       int i = 0;
       for (; i + 2 < ntiles; i += 2) {
         okb = load_tile(b + W, kb, vb);
@@ -360,6 +455,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       emit(h, d, num, den, mx);
     }
   }
+
 }
 
 // Merge the partitions of every (sequence, query head) that was split.
@@ -406,11 +502,29 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeParams p)
 }
 
 // ---------------------------------------------------------------------------------------
+// Waves per work-group of the partition kernel.  A whole-context pass (one work-group per
+// (KV head, sequence)) runs 8 waves, so one work-group fills a CU and, with the
+// longest-first order, the dispatcher hands out the remaining shorter contexts to whichever
+// CU frees up first.  A split pass has many short work-groups: 4 waves each.
+#ifndef PA_DECODE_WAVES_WHOLE
+#define PA_DECODE_WAVES_WHOLE 8
+#endif
+#ifndef PA_DECODE_WAVES_SPLIT
+#define PA_DECODE_WAVES_SPLIT 4
+#endif
+
 template <int KV, int D, int G>
 static hipError_t launch_parts_kv_d_g(const DecodeParams& p, int num_seqs, hipStream_t stream) {
-  constexpr int W = 4;
-  dim3 grid(p.max_parts, p.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((decode_partition_kernel<KV, D, G, W>), grid, dim3(64 * W), 0, stream, p);
+  // KV head fastest: consecutive work-groups go to different XCDs, and with 8 KV heads
+  // each XCD streams one head of every sequence (equal shares whatever the lengths).
+  dim3 grid(p.num_kv_heads, p.max_parts, num_seqs);
+  if (p.max_parts <= 1) {
+    constexpr int W = PA_DECODE_WAVES_WHOLE;
+    hipLaunchKernelGGL((decode_partition_kernel<KV, D, G, W>), grid, dim3(64 * W), 0, stream, p);
+  } else {
+    constexpr int W = PA_DECODE_WAVES_SPLIT;
+    hipLaunchKernelGGL((decode_partition_kernel<KV, D, G, W>), grid, dim3(64 * W), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -187,21 +187,33 @@ __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit
 __device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
 // ---------------------------------------------------------------------------
-// vector loads of N dwords (N = 1, 2, 4, 8)
+// vector loads of N dwords (N = 1, 2, 4, 8); NT marks streaming data that is read once
+// (the KV tiles), so it does not displace reusable lines in L2 / Infinity Cache.
 // ---------------------------------------------------------------------------
-template <int N>
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <typename V, bool NT>
+__device__ __forceinline__ V ld(const void* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+  else
+    return *reinterpret_cast<const V*>(p);
+}
+
+template <int N, bool NT = false>
 __device__ __forceinline__ void load_dw(uint32_t (&d)[N], const void* p) {
   if constexpr (N == 1) {
-    d[0] = *reinterpret_cast<const uint32_t*>(p);
+    d[0] = ld<uint32_t, NT>(p);
   } else if constexpr (N == 2) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
+    u32x2_t v = ld<u32x2_t, NT>(p);
     d[0] = v.x; d[1] = v.y;
   } else if constexpr (N == 4) {
-    uint4 v = *reinterpret_cast<const uint4*>(p);
+    u32x4_t v = ld<u32x4_t, NT>(p);
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
   } else {
-    uint4 v = reinterpret_cast<const uint4*>(p)[0];
-    uint4 w = reinterpret_cast<const uint4*>(p)[1];
+    u32x4_t v = ld<u32x4_t, NT>(p);
+    u32x4_t w = ld<u32x4_t, NT>(reinterpret_cast<const uint8_t*>(p) + 16);
     d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
     d[4] = w.x; d[5] = w.y; d[6] = w.z; d[7] = w.w;
   }

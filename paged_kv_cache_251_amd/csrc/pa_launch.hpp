@@ -27,6 +27,17 @@ struct DecodeParams {
   int32_t partition_tokens;  // 0: one pass per context
   int32_t max_parts;         // grid.x: partitions of the longest context (1 if unsplit)
   float scale_log2;          // scale * log2(e)
+  // Append mode (non-null key_new): each sequence's newest token (position L-1) has its
+  // K/V row [num_kv_heads][D] (query dtype) in key_new/value_new; the work-group whose
+  // partition holds that position writes it into the pools and uses it directly.
+  const void* key_new;
+  const void* value_new;
+  void* key_cache_w;
+  void* value_cache_w;
+  // Longest-first order: grid z is a rank, not a sequence index; every work-group ranks
+  // the sequences by context length (ties by index) and takes the one with its rank, so
+  // the dispatcher hands out long contexts first (greedy longest-processing-time).
+  int32_t longest_first;
 };
 
 // Partition pass: a sequence with one partition gets its output row; a split one gets

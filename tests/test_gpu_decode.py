@@ -171,3 +171,52 @@ def test_invalid_table_entries_are_skipped_without_fault():
     assert torch.all(out2[0].float() == 0)
     assert torch.equal(out2[1].view(torch.int16), pa.paged_attention_decode(
         b.q, b.pk, b.pv, b.tables, b.lens, w.max_context_len, w.scale, partition_size=16)[1].view(torch.int16))
+
+
+# ---------------------------------------------------------------- fused append + decode
+def _append_case(w, part):
+    from workloads import STORAGE, seq_kv
+
+    a = DeviceBatch(w, phases=("cached",))
+    b = DeviceBatch(w, phases=("cached",))
+    # the newest row of every sequence ([N, Hkv, D]; zeros for an empty context, not read)
+    kn = np.zeros((w.num_seqs, w.num_kv_heads, w.head_dim), STORAGE[w.src_dtype])
+    vn = np.zeros_like(kn)
+    for s in range(w.num_seqs):
+        if w.context_lens[s] > 0:
+            ks, vs = seq_kv(w, s)
+            kn[s], vn[s] = ks[-1], vs[-1]
+    k = to_device(kn, w.src_dtype)
+    v = to_device(vn, w.src_dtype)
+    a.write("new")
+    out_sep = a.decode(part)
+    out_fused = pa.paged_attention_decode_append(b.q, k, v, b.pk, b.pv, b.tables, b.lens, w.max_context_len,
+                                                 w.scale, partition_size=part)
+    return a, b, out_sep, out_fused
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32) if t.dtype == torch.float32 else t
+
+
+@pytest.mark.parametrize("idx,part", [(1, 0), (1, 32), (2, -1), (2, 0), (2, 512)])
+def test_append_is_bit_identical_to_write_then_decode(idx, part):
+    w = make_config(idx)
+    a, b, out_sep, out_fused = _append_case(w, part)
+    assert torch.equal(_bits(out_sep), _bits(out_fused))
+    assert torch.equal(_bits(a.pk), _bits(b.pk)) and torch.equal(_bits(a.pv), _bits(b.pv))
+
+
+@pytest.mark.parametrize("dtype,D,G", [("e5m2", 128, 4), ("e5m2", 64, 8), ("bf16", 64, 2), ("f32", 128, 4)])
+def test_append_edge_lengths_against_oracle(dtype, D, G):
+    qd = "f32" if dtype == "f32" else "bf16"
+    w = make_workload([1, 2, 16, 17, 32, 33, 300, 513, 0], num_q_heads=2 * G, num_kv_heads=2, head_dim=D, q_dtype=qd,
+                      src_dtype=qd, kv_dtype=dtype, seed=zlib.crc32(f"app{dtype}{D}{G}".encode()) % 1000)
+    pk, pv = oracle_pools(w)
+    ref = _oracle_decode(w, pk, pv)
+    for part in (0, 256):
+        a, b, out_sep, out_fused = _append_case(w, part)
+        assert torch.equal(_bits(out_sep), _bits(out_fused))
+        assert np.array_equal(canonical(b.pk, dtype).view(np.uint8), pk.view(np.uint8))
+        assert np.array_equal(canonical(b.pv, dtype).view(np.uint8), pv.view(np.uint8))
+        assert_close(out_f64(out_fused, qd), ref, qd, f"append {dtype} D{D} G{G} partition {part}")

@@ -9,6 +9,7 @@ compared (``oracle/`` on the CPU, ``libpagedattn`` on the GPU).
 from .generate import (  # noqa: F401
     CONFIG_NAMES,
     POISON_BITS,
+    STORAGE,
     Workload,
     WritePlan,
     make_config,

@@ -313,7 +313,7 @@ def write_plan(w: Workload, phase: str = "all", seqs=None) -> WritePlan:
         starts = np.minimum(starts, ends)
     elif phase == "new":
         ends = lens.copy()
-        starts = lens - w.q_lens
+        starts = np.maximum(lens - w.q_lens, 0)
     else:
         raise ValueError(phase)
     sel = range(w.num_seqs) if seqs is None else seqs
