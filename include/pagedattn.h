@@ -243,6 +243,35 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
                                           pa_dtype_t kv_dtype, int32_t partition_size, int32_t flags,
                                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * paged_attention_varlen -- one continuous-batching step: prefill chunks and decode tokens
+ * packed into one 1-D token stream without padding.  [CI Continuous Batching: prefill and
+ * decode are kept apart but no padding is added, the operators take 1-D input; OPT 2.3.2:
+ * prefill is GEMM-bound, decode GEMV-bound]
+ *
+ * Sequence s owns query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1: its n_s newest tokens,
+ * whose K/V rows must already be in the cache (kv_cache_write first).  Its context holds
+ * L = context_lens[s] tokens, the new ones included, so query row i of the sequence sits at
+ * position L - n_s + i.  With causal = 1 it attends keys 0 .. L-n_s+i (the mask aligned to
+ * the end of the context); with causal = 0 every query row attends all L keys.
+ *   out, query    [total_q][num_kv_heads*gqa_group][head_dim], bf16
+ *   cu_seqlens_q  int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[0] = 0,
+ *                 cu_seqlens_q[num_seqs] = total_q; max_q_len >= every n_s
+ *   other arguments as in paged_attention_decode; the workspace is sized by
+ *   paged_attention_workspace_size(num_seqs, ...) and serves the 1-token rows.
+ * Rows with n_s = 1 go through the decode kernels (split-KV when partition_size asks for
+ * it); rows of sequences with n_s >= 2 through MFMA tiles.  Supported: bf16 query and cache.
+ * A row whose position is negative (n_s > L) sees no key and comes out zero.
+ */
+pa_status_t paged_attention_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                   int32_t total_q, int32_t max_q_len, int32_t num_kv_heads, int32_t gqa_group,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                                   float scale, int32_t causal, pa_dtype_t q_dtype, pa_dtype_t kv_dtype,
+                                   int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     lib,
     paged_attention_decode,
     paged_attention_decode_append,
+    paged_attention_varlen,
     slot_mapping,
     workspace_size,
 )

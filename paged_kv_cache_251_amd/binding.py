@@ -41,6 +41,9 @@ SIGNATURES = {
     "paged_attention_decode_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _i32,
                                                      _i32, _vp, _sz, _vp]),
+    "paged_attention_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                              _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, ctypes.c_int, _i32,
+                                              _vp, _sz, _vp]),
 }
 PA_APPEND_SKIP_REDUCE = 1
 
@@ -225,4 +228,35 @@ def paged_attention_decode_append(query: torch.Tensor, key: torch.Tensor, value:
         block_tables.shape[1], _ptr(context_lens), n, hkv, g, d, bs, nb, max_context_len, scale, dtype_code(query),
         dtype_code(key_cache), partition_size, 0, _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream()))
+    return out
+
+
+def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                           cu_seqlens_q: torch.Tensor, context_lens: torch.Tensor, block_tables: torch.Tensor,
+                           max_q_len: int, max_context_len: int, scale: float, causal: bool = True,
+                           partition_size: int = -1, out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed prefill + decode step: query [total_q, Hq, D] (``paged_attention_varlen``)."""
+    _dev(query, key_cache, value_cache, cu_seqlens_q, context_lens, block_tables)
+    _int32(cu_seqlens_q, context_lens, block_tables)
+    total_q, hq, d = query.shape
+    nb, hkv, bs, _ = key_cache.shape
+    n = context_lens.shape[0]
+    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    _expect(key_cache.shape[3] == d and hq % hkv == 0, "query and pools disagree on D / heads")
+    _expect(cu_seqlens_q.shape == (n + 1,) and block_tables.dim() == 2 and block_tables.shape[0] == n,
+            "cu_seqlens_q [N+1], context_lens [N], block_tables [N, max_blocks]")
+    g = hq // hkv
+    if out is None:
+        out = torch.empty_like(query)
+    _dev(out)
+    _expect(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    need = workspace_size(n, hkv, g, d, max_context_len, partition_size)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = alloc_workspace(need, query.device)
+    _check("paged_attention_varlen", lib().paged_attention_varlen(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(cu_seqlens_q), _ptr(context_lens),
+        _ptr(block_tables), block_tables.shape[1], n, total_q, max_q_len, hkv, g, d, bs, nb, max_context_len, scale,
+        1 if causal else 0, dtype_code(query), dtype_code(key_cache), partition_size, _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream()))
     return out

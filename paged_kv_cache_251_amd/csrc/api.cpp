@@ -369,4 +369,37 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
   return device_status(e, fn);
 }
 
+pa_status_t paged_attention_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
+                                   const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                   const int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                                   int32_t total_q, int32_t max_q_len, int32_t num_kv_heads, int32_t gqa_group,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                                   float scale, int32_t causal, pa_dtype_t q_dtype, pa_dtype_t kv_dtype,
+                                   int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  const char* fn = "paged_attention_varlen";
+  if (total_q < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: total_q %d < 0", fn, total_q);
+  if (max_q_len < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: max_q_len %d < 0", fn, max_q_len);
+  if (max_q_len > total_q) return fail(PA_ERR_INVALID_ARGUMENT, "%s: max_q_len %d > total_q %d", fn, max_q_len, total_q);
+  if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARGUMENT, "%s: causal must be 0 or 1", fn);
+  pa::DecodeParams p;
+  pa_status_t st = prepare_decode(fn, p, out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                                  context_lens, num_seqs, num_kv_heads, gqa_group, head_dim, block_size, num_blocks,
+                                  max_context_len, scale, q_dtype, kv_dtype, partition_size, workspace,
+                                  workspace_bytes, true);
+  if (st != PA_OK) return st;
+  if (q_dtype != PA_BF16 || kv_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: packed batches take bf16 queries and a bf16 cache", fn);
+  if (num_seqs == 0 || total_q == 0) return ok();
+  if (!cu_seqlens_q || !aligned(cu_seqlens_q, 4)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens_q", fn);
+  const int64_t prefill_tiles = (static_cast<int64_t>(max_q_len) * gqa_group + 127) / 128;
+  if (prefill_tiles > kMaxGridYZ) return fail(PA_ERR_UNSUPPORTED, "%s: max_q_len %d too large", fn, max_q_len);
+  p.cu_q = cu_seqlens_q;
+  p.causal = causal;
+  hipError_t e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
+  if (e == hipSuccess) e = pa::launch_decode_reduce(p, true, head_dim, num_kv_heads * gqa_group, num_seqs, stream);
+  if (e == hipSuccess) e = pa::launch_varlen_prefill(p, head_dim, gqa_group, num_seqs, max_q_len, stream);
+  return device_status(e, fn);
+}
+
 }  // extern "C"

@@ -38,6 +38,7 @@ struct DecodeParams {
   // the sequences by context length (ties by index) and takes the one with its rank, so
   // the dispatcher hands out long contexts first (greedy longest-processing-time).
   int32_t longest_first;
+  int32_t causal;  // packed (varlen) batches: mask aligned to the end of each context
 };
 
 // Partition pass: a sequence with one partition gets its output row; a split one gets
@@ -47,6 +48,10 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head
 // Merge pass over the split sequences (no-op when p.max_parts <= 1).
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
                                 hipStream_t stream);
+
+// Prefill rows (sequences with >= 2 query tokens) of a packed batch, on MFMA.
+hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
+                                 hipStream_t stream);
 
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* cu, const int32_t* end_pos,
                                const int32_t* tables, int32_t max_blocks, int32_t num_seqs,

@@ -1,0 +1,259 @@
+// Prefill part of a packed (varlen) step on gfx950 MFMA.
+//
+// A packed batch holds, per sequence, the n newest tokens of a context of L tokens
+// (Colossal-Inference release post, "连续批量化算法 (Continuous Batching)": prefill and
+// decode tokens go through the same 1-D operators without padding).  Their K/V rows are
+// already in the cache.  Query token i of the sequence sits at position L-n+i and, when
+// causal, sees keys 0..L-n+i (the mask aligned to the end of the context).  Sequences with
+// n = 1 are decode rows and go through the decode kernel; this kernel takes n >= 2, where
+// QK^T and PV are dense contractions (LLM inference optimisation overview, 2.3.2: prefill is
+// GEMM-bound).
+//
+// Work-group = 4 waves = 128 query rows of one KV head: row r is (token i0 + r / G, head r % G),
+// so the G heads that share the KV head share every K/V tile.  Each wave owns two 16-row
+// tiles.  Per 64-key tile:
+//   S^T[keys][rows] = K[keys][D] . Q^T[D][rows]     v_mfma_f32_16x16x32_bf16, A = K from LDS
+//                                                    (row-major), B = Q from registers
+//   O^T[D][rows]  += V^T[D][keys] . P^T[keys][rows]  A = V^T from LDS (stored transposed),
+//                                                    B = P straight from the S^T accumulators
+// With S^T, lane l holds 4 consecutive keys of query row l%16 per 16-key tile; two tiles give
+// the 8 keys the B operand of the PV step needs (keys 4j..4j+3 and 16+4j..16+4j+3 for lane
+// group j = l/16), and V^T is read with the same key order, so P never goes through LDS.
+// Every accumulator of lane l belongs to row l%16: the online-softmax rescale is per lane.
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr float kTauPrefill = 8.0f;
+
+__device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void varlen_prefill_kernel(const DecodeParams p) {
+  constexpr int W = 4, NT = 2;            // waves; 16-row MFMA tiles per wave
+  constexpr int ROWS = W * NT * 16;       // query rows per work-group
+  constexpr int TOKW = ROWS / G;          // tokens per work-group
+  constexpr int KT = 64;                  // keys per LDS tile (4 cache blocks)
+  constexpr int KS = D / 32;              // MFMA k-steps over head_dim
+  constexpr int DT = D / 16;              // 16-wide output tiles over head_dim
+  constexpr int KP = D + 8;               // K row pitch in LDS (bf16 elements)
+  constexpr int VP = KT + 8;              // V^T row pitch in LDS (keys)
+  constexpr int CH = D / 8;               // 16-byte chunks per K/V row
+  constexpr int LOADS = KT * CH / 256;    // 16-byte chunks per thread per tile (K and V each)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;  // MFMA row / column-in-tile and lane group
+  const int g = blockIdx.x, tile = blockIdx.y, s = blockIdx.z;
+  const int hq = p.num_kv_heads * G;
+
+  const int a = load_invariant(p.cu_q + s);
+  const int n = load_invariant(p.cu_q + s + 1) - a;
+  if (n <= 1) return;  // decode rows: the decode kernel
+  const int i0 = tile * TOKW;
+  if (i0 >= n) return;
+  int L = load_invariant(p.context_lens + s);
+  L = L < 0 ? 0 : L;
+  L = L > p.max_context_len ? p.max_context_len : L;
+  L = L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
+  const bool causal = p.causal != 0;
+  // keys any row of this work-group may see
+  const int last_tok = min(n, i0 + TOKW) - 1;
+  int kv_end = causal ? L - n + last_tok + 1 : L;
+  kv_end = kv_end < 0 ? 0 : (kv_end > L ? L : kv_end);
+
+  // ---- query rows of this lane (B operand of S^T = K Q^T) -------------------------------
+  int tok[NT], lim[NT];
+  uint4 qb[NT][KS];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int r = wave * (NT * 16) + j * 16 + lr;
+    tok[j] = i0 + r / G;
+    const int h = r % G;
+    const bool ok = tok[j] < n;
+    lim[j] = ok ? (causal ? min(L, L - n + tok[j] + 1) : L) : 0;  // keys [0, lim) visible
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(p.query) + ((size_t)(a + (ok ? tok[j] : 0)) * hq + (size_t)g * G + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg);
+      qb[j][kk] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  float m_run[NT], l_run[NT];
+  f32x4_t oacc[NT][DT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    m_run[j] = -__builtin_inff();
+    l_run[j] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[j][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.key_cache);
+  const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.value_cache);
+
+  const int ntiles = (kv_end + KT - 1) / KT;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    // ---- stage the K tile (row-major) and the V tile (transposed) in LDS ------------------
+    uint4 kreg[LOADS], vreg[LOADS];
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int q = tid + 256 * u;
+      const int key = q / CH, c = q % CH;
+      const int kidx = kt * KT + key;
+      bool ok = kidx < kv_end;
+      int phys = ok ? load_invariant(table + kidx / 16) : 0;
+      ok = ok && phys >= 0 && phys < p.num_blocks;
+      phys = ok ? phys : 0;
+      const size_t off = (((size_t)phys * p.num_kv_heads + g) * 16 + (kidx & 15)) * D + (size_t)c * 8;
+      const uint4 kv = *reinterpret_cast<const uint4*>(kc + off);
+      const uint4 vv = *reinterpret_cast<const uint4*>(vc + off);
+      kreg[u] = ok ? kv : make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN: zero them
+      vreg[u] = ok ? vv : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // the previous tile has been consumed
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int q = tid + 256 * u;
+      const int key = q / CH, c = q % CH;
+      *reinterpret_cast<uint4*>(Ks + key * KP + c * 8) = kreg[u];
+      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(c * 8 + 2 * e) * VP + key] = (uint16_t)(w[e] & 0xFFFFu);
+        Vt[(c * 8 + 2 * e + 1) * VP + key] = (uint16_t)(w[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for the tile's 4 groups of 16 keys ------------------------------------
+    f32x4_t sacc[NT][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) sacc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(Ks + (m * 16 + lr) * KP + 32 * kk + 8 * lg);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) sacc[j][m] = mfma_16x16x32(ka, qb[j][kk], sacc[j][m]);
+      }
+    }
+
+    // ---- mask, online softmax (threshold rescale), P in the B-operand key order -----------
+    uint4 pb[NT][2];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      float sv[4][4];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt * KT + m * 16 + 4 * lg + i;
+          sv[m][i] = key < lim[j] ? sacc[j][m][i] * p.scale_log2 : -__builtin_inff();
+          mx = fmaxf(mx, sv[m][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > m_run[j] + kTauPrefill;
+      if (__any(need)) {
+        const float mn = need ? mx : m_run[j];
+        const float alpha = need ? fast_exp2(m_run[j] - mn) : 1.f;
+        l_run[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[j][dt] *= alpha;
+        m_run[j] = mn;
+      }
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = sv[m][i] == -__builtin_inff() ? 0.f : fast_exp2(sv[m][i] - m_run[j]);
+        const uint32_t b0 = f32_to_bf16_rne(pv[0]), b1 = f32_to_bf16_rne(pv[1]);
+        const uint32_t b2 = f32_to_bf16_rne(pv[2]), b3 = f32_to_bf16_rne(pv[3]);
+        // the denominator sums the same rounded weights the numerator uses
+        l_run[j] += bf16lo(b0) + bf16lo(b1) + bf16lo(b2) + bf16lo(b3);
+        pk[m][0] = b0 | (b1 << 16);
+        pk[m][1] = b2 | (b3 << 16);
+      }
+      pb[j][0] = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);  // keys 4lg.. , 16+4lg..
+      pb[j][1] = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);  // keys 32+4lg.., 48+4lg..
+    }
+
+    // ---- O^T += V^T P^T --------------------------------------------------------------------
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint16_t* vrow = Vt + (dt * 16 + lr) * VP + ks * 32 + 4 * lg;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) oacc[j][dt] = mfma_16x16x32(va, pb[j][ks], oacc[j][dt]);
+      }
+    }
+  }
+
+  // ---- normalise and store: lane l holds dims dt*16 + 4*lg .. +3 of row l%16 --------------
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    float lt = l_run[j];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int r = wave * (NT * 16) + j * 16 + lr;
+    if (tok[j] >= n) continue;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(a + tok[j]) * hq + (size_t)g * G + r % G) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t w0 = f32_to_bf16_rne(oacc[j][dt][0] * inv) | (f32_to_bf16_rne(oacc[j][dt][1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(oacc[j][dt][2] * inv) | (f32_to_bf16_rne(oacc[j][dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * lg) = make_uint2(w0, w1);
+    }
+  }
+}
+
+template <int D, int G>
+static hipError_t launch_prefill_dg(const DecodeParams& p, int num_seqs, int max_q_len, hipStream_t stream) {
+  constexpr int TOKW = 128 / G;
+  dim3 grid(p.num_kv_heads, (max_q_len + TOKW - 1) / TOKW, num_seqs);
+  hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const DecodeParams& p, int gqa, int num_seqs, int max_q_len, hipStream_t stream) {
+  switch (gqa) {
+    case 1: return launch_prefill_dg<D, 1>(p, num_seqs, max_q_len, stream);
+    case 2: return launch_prefill_dg<D, 2>(p, num_seqs, max_q_len, stream);
+    case 4: return launch_prefill_dg<D, 4>(p, num_seqs, max_q_len, stream);
+    case 8: return launch_prefill_dg<D, 8>(p, num_seqs, max_q_len, stream);
+    case 16: return launch_prefill_dg<D, 16>(p, num_seqs, max_q_len, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
+                                 hipStream_t stream) {
+  if (max_q_len <= 1) return hipSuccess;  // no sequence has two or more query tokens
+  if (head_dim == 128) return launch_prefill_d<128>(p, gqa, num_seqs, max_q_len, stream);
+  if (head_dim == 64) return launch_prefill_d<64>(p, gqa, num_seqs, max_q_len, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
