@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload 1-4 (decode)")
+    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (1-4 decode, 5 packed prefill + decode)")
     ap.add_argument("--replicas", type=int, default=0, help="resident batches to rotate (0: enough for >= 1.2 GB)")
     ap.add_argument("--partition", type=int, default=None, help="partition tokens (default: workload's, else auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
@@ -119,6 +119,169 @@ class Batch:
         self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * d * 2 * KV_BYTES[w.kv_dtype]
 
 
+class VarlenBatch:
+    """One resident packed batch (prefill chunks first, then decode tokens): pools hold every
+    sequence's history; a step writes the new tokens' K/V and attends."""
+
+    def __init__(self, w, partition, pa, torch, to_dev):
+        from workloads import POISON_BITS, queries, write_plan
+
+        dev = "cuda:0"
+        self.w = w
+        self.tables = torch.from_numpy(w.block_tables).to(dev)
+        self.lens = torch.from_numpy(w.context_lens).to(dev)
+        shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        self.pk = torch.full(shape, POISON_BITS["bf16"], dtype=torch.int16, device=dev).view(torch.bfloat16)
+        self.pv = self.pk.clone()
+        hist = write_plan(w, "cached")
+        slots = pa.slot_mapping(torch.from_numpy(hist.cu).to(dev), torch.from_numpy(hist.end_pos).to(dev),
+                                self.tables, hist.num_tokens, w.num_blocks)
+        pa.kv_cache_write(to_dev(hist.k, "bf16"), to_dev(hist.v, "bf16"), self.pk, self.pv, slots)
+        new = write_plan(w, "new")
+        self.cu_new = torch.from_numpy(new.cu).to(dev)
+        self.end_new = torch.from_numpy(new.end_pos).to(dev)
+        self.knew, self.vnew = to_dev(new.k, "bf16"), to_dev(new.v, "bf16")
+        self.ntok = new.num_tokens
+        self.slots = torch.empty(self.ntok, dtype=torch.int32, device=dev)
+        self.q = to_dev(queries(w), "bf16")
+        self.out = torch.empty_like(self.q)
+        self.cu_q = torch.from_numpy(w.cu_seqlens_q).to(dev)
+        n, hkv, g, d, bs, nb = w.num_seqs, w.num_kv_heads, w.gqa_group, w.head_dim, w.block_size, w.num_blocks
+        mb, ml = w.max_blocks_per_seq, w.max_context_len
+        n_pre = int((w.q_lens > 1).sum())  # prefill chunks are packed first
+        # the full batch and the prefill-only / decode-only sub-batches may resolve differently
+        need = max(pa.workspace_size(k, hkv, g, d, ml, partition) for k in (n, n_pre, n - n_pre) if k > 0)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        self.resolved = partition if partition >= 0 else pa.auto_partition(n, hkv, g, d, ml)
+        P = lambda t: t.data_ptr()
+        bf = pa.binding.PA_BF16
+        self.args_slot = (P(self.slots), P(self.cu_new), P(self.end_new), P(self.tables), mb, n, self.ntok, bs, nb)
+        self.args_write = (P(self.knew), P(self.vnew), P(self.pk), P(self.pv), P(self.slots), self.ntok, hkv, d, bs,
+                           nb, bf, bf)
+
+        def varlen_args(s0, s1):
+            rows0 = int(w.cu_seqlens_q[s0])
+            cu = torch.from_numpy((w.cu_seqlens_q[s0 : s1 + 1] - rows0).astype("int32")).to(dev)
+            self._keep.append(cu)
+            qlen = int(w.q_lens[s0:s1].max())
+            qoff = rows0 * w.num_q_heads * d * 2
+            return (P(self.out) + qoff, P(self.q) + qoff, P(self.pk), P(self.pv), P(cu), P(self.lens) + 4 * s0,
+                    P(self.tables) + 4 * mb * s0, mb, s1 - s0, int(w.q_lens[s0:s1].sum()), qlen, hkv, g, d, bs, nb,
+                    ml, w.scale, 1, bf, bf, partition, P(self.ws), self.ws.numel())
+
+        self._keep = []
+        self.args_varlen = varlen_args(0, n)
+        self.args_prefill_only = varlen_args(0, n_pre)
+        self.args_decode_only = varlen_args(n_pre, n)
+        self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * d * 2 * 2
+        self.decode_kv_bytes = int(w.context_lens[n_pre:].astype("int64").sum()) * hkv * d * 2 * 2
+        pos = [(int(L) - int(qn) + i + 1) for L, qn in zip(w.context_lens[:n_pre], w.q_lens[:n_pre]) for i in range(qn)]
+        self.prefill_flops = 4 * w.num_q_heads * d * int(sum(max(0, x) for x in pos))
+
+
+def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
+    """The packed continuous-batching step (prefill chunks + decode tokens)."""
+    from workloads import CONFIG_NAMES, make_config
+
+    w0 = make_config(args.config)
+    partition = args.partition if args.partition is not None else -1
+    reps = args.replicas or 4
+    batches = [VarlenBatch(w0 if r == 0 else make_config(args.config, replica=r), partition, pa, torch, to_dev)
+               for r in range(reps)]
+    torch.cuda.synchronize()
+
+    def step(b):
+        check(lib.paged_kv_slot_mapping(*b.args_slot, sh), "slot mapping")
+        check(lib.kv_cache_write(*b.args_write, sh), "cache write")
+        check(lib.paged_attention_varlen(*b.args_varlen, sh), "varlen")
+
+    def timed(call, with_events):
+        for i in range(args.warmup):
+            call(batches[i % reps])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] if with_events else None
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(args.steps):
+            if with_events:
+                evs[i][0].record(stream)
+            call(batches[i % reps])
+            if with_events:
+                evs[i][1].record(stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        kern = float(np.mean([a.elapsed_time(b) for a, b in evs])) if with_events else None
+        return start.elapsed_time(stop) / args.steps, kern
+
+    dec = lambda b: check(lib.paged_attention_varlen(*b.args_decode_only, sh), "varlen decode rows")
+    pre = lambda b: check(lib.paged_attention_varlen(*b.args_prefill_only, sh), "varlen prefill rows")
+    _, dec_ms = timed(dec, True)
+    _, pre_ms = timed(pre, True)
+    ms_step, _ = timed(step, False)
+    step_bytes = float(np.mean([batches[i % reps].kv_bytes for i in range(args.steps)]))
+    dec_bytes = float(np.mean([batches[i % reps].decode_kv_bytes for i in range(args.steps)]))
+    pre_flops = float(np.mean([batches[i % reps].prefill_flops for i in range(args.steps)]))
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    pre_tflops = pre_flops / (pre_ms * 1e-3) / 1e12
+    cpu = None if args.no_cpu_baseline else cpu_baseline_varlen(batches[0].w, args.cpu_seconds)
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": CONFIG_NAMES[args.config],
+            "num_seqs": w0.num_seqs,
+            "prefill_chunks": int((w0.q_lens > 1).sum()),
+            "total_q": w0.total_q,
+            "num_q_heads": w0.num_q_heads,
+            "num_kv_heads": w0.num_kv_heads,
+            "head_dim": w0.head_dim,
+            "block_size": w0.block_size,
+            "partition_tokens": batches[0].resolved,
+            "resident_batches": reps,
+            "step": "slot mapping + cache write of every new token + paged_attention_varlen "
+                    "(decode rows on the decode kernel, prefill rows on MFMA tiles)",
+        },
+        "seq_steps_per_s": round(w0.num_seqs / (ms_step * 1e-3), 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": int(step_bytes),
+        "roofline": {
+            "kernel": "decode_partition_kernel (1-token rows of the packed batch)",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dec_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(dec_bytes),
+        },
+        "prefill_mfma": {
+            "kernel": "varlen_prefill_kernel (prefill rows alone; the call also issues an empty decode launch)",
+            "bound": "mfma",
+            "achieved": round(pre_tflops, 2),
+            "peak": 2500.0,
+            "unit": "TFLOP/s",
+            "frac": round(pre_tflops / 2500.0, 4),
+            "avg_call_us": round(pre_ms * 1e3, 3),
+            "flops_per_call": int(pre_flops),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -142,8 +305,17 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(raw, np.float32)).to("cuda:0")
         return torch.from_numpy(np.ascontiguousarray(raw, np.uint16).view(np.int16)).to("cuda:0").view(torch.bfloat16)
 
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def check(st, fn):
+        if st != 0:
+            raise RuntimeError(f"{fn}: {lib.pa_last_error().decode()}")
+
     w0 = make_config(args.config)
-    assert w0.is_decode, "bench.py times the decode workloads (1-4)"
+    if not w0.is_decode:
+        bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check)
+        return
     partition = args.partition if args.partition is not None else (w0.partition_size or -1)
     pool_bytes = w0.num_blocks * w0.num_kv_heads * 16 * w0.head_dim * 2 * KV_BYTES[w0.kv_dtype]
     reps = args.replicas or max(2, min(8, -(-1_200_000_000 // pool_bytes)))
@@ -153,13 +325,6 @@ def main():
     torch.cuda.synchronize()
     print(f"# setup: {reps} resident batches of {CONFIG_NAMES[args.config]} in {time.perf_counter() - t_setup:.1f} s",
           file=sys.stderr, flush=True)
-
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-
-    def check(st, fn):
-        if st != 0:
-            raise RuntimeError(f"{fn}: {lib.pa_last_error().decode()}")
 
     def step(b, ev=None):
         """Fused step: append + attend in one launch (+ the reduce kernel for split contexts)."""
@@ -338,6 +503,48 @@ def cpu_baseline(w, budget_s):
         "kind": "oracle",
         "sample": f"{done_seqs} sequence-steps cycling over the {w.num_seqs} sequences of the timed workload "
                   f"(slot mapping, cache write of the newest token, float64 attention each), {t_used:.1f} s",
+    }
+
+
+def cpu_baseline_varlen(w, budget_s):
+    """The oracle on the packed step: each pass takes the next sequences through the oracle's
+    slot mapping, cache write of their new tokens and causal paged attention."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import POISON_BITS, queries, write_plan
+
+    q = queries(w)
+    done_seqs, done_bytes, t_used, s0 = 0, 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while t_used < budget_s:
+            sel = [(s0 + i) % w.num_seqs for i in range(8)]
+            pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, "bf16", POISON_BITS["bf16"])
+            pv = pk.copy()
+            hist = write_plan(w, "cached", sel)
+            hs = oracle.slot_mapping(w.block_tables, hist.counts, hist.end_pos, w.block_size)
+            oracle.cache_write(pk, hist.k, hs, "bf16", "bf16", w.block_size)
+            oracle.cache_write(pv, hist.v, hs, "bf16", "bf16", w.block_size)
+            new = write_plan(w, "new", sel)
+            t0 = time.perf_counter()
+            ns = oracle.slot_mapping(w.block_tables, new.counts, new.end_pos, w.block_size)
+            oracle.cache_write(pk, new.k, ns, "bf16", "bf16", w.block_size)
+            oracle.cache_write(pv, new.v, ns, "bf16", "bf16", w.block_size)
+            oracle.paged_varlen(pk, pv, "bf16", q, "bf16", w.cu_seqlens_q, w.block_tables, w.context_lens,
+                                w.block_size, w.scale, causal=True, seqs=sel)
+            t_used += time.perf_counter() - t0
+            done_seqs += len(sel)
+            done_bytes += int(w.context_lens[sel].astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 4
+            s0 += 8
+    return {
+        "value": round(done_bytes / t_used / 1e9, 4),
+        "unit": "GB/s",
+        "seq_steps_per_s": round(done_seqs / t_used, 3),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done_seqs} sequence-steps cycling over the {w.num_seqs} sequences of the packed workload "
+                  f"(slot mapping, cache write of the new tokens, causal float64 attention each), {t_used:.1f} s",
     }
 
 

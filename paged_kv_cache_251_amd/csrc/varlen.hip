@@ -14,11 +14,15 @@
 // tiles.  Per 64-key tile:
 //   S^T[keys][rows] = K[keys][D] . Q^T[D][rows]     v_mfma_f32_16x16x32_bf16, A = K from LDS
 //                                                    (row-major), B = Q from registers
-//   O^T[D][rows]  += V^T[D][keys] . P^T[keys][rows]  A = V^T from LDS (stored transposed),
-//                                                    B = P straight from the S^T accumulators
+//   O^T[D][rows]  += V^T[D][keys] . P^T[keys][rows]  A = V^T read from the row-major V tile
+//                                                    with ds_read_b64_tr_b16, B = P straight
+//                                                    from the S^T accumulators
 // With S^T, lane l holds 4 consecutive keys of query row l%16 per 16-key tile; two tiles give
 // the 8 keys the B operand of the PV step needs (keys 4j..4j+3 and 16+4j..16+4j+3 for lane
-// group j = l/16), and V^T is read with the same key order, so P never goes through LDS.
+// group j = l/16), and V^T is read in the same key order, so P never goes through LDS.
+// ds_read_b64_tr_b16 (checked on the device): within each 16-lane group, lane i's j-th 16-bit
+// result is element i%4 of the 8 bytes read by lane 4j + i/4.  So if lane k of the group reads
+// dims 4(k%4)..+3 of key k/4, lane i receives dim i of the 4 keys -- a column of V.
 // Every accumulator of lane l belongs to row l%16: the online-softmax rescale is per lane.
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
@@ -27,8 +31,16 @@ namespace pa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr float kTauPrefill = 8.0f;
+
+// ds_read_b64_tr_b16 on an LDS address (see the lane mapping above)
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
 
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -36,7 +48,7 @@ __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b,
 }
 
 template <int D, int G>
-__global__ __launch_bounds__(256) void varlen_prefill_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodeParams p) {
   constexpr int W = 4, NT = 2;            // waves; 16-row MFMA tiles per wave
   constexpr int ROWS = W * NT * 16;       // query rows per work-group
   constexpr int TOKW = ROWS / G;          // tokens per work-group
@@ -44,16 +56,17 @@ __global__ __launch_bounds__(256) void varlen_prefill_kernel(const DecodeParams 
   constexpr int KS = D / 32;              // MFMA k-steps over head_dim
   constexpr int DT = D / 16;              // 16-wide output tiles over head_dim
   constexpr int KP = D + 8;               // K row pitch in LDS (bf16 elements)
-  constexpr int VP = KT + 8;              // V^T row pitch in LDS (keys)
+  constexpr int VP = D + 16;              // V row pitch in LDS: 4 rows x 4 chunks hit distinct banks
   constexpr int CH = D / 8;               // 16-byte chunks per K/V row
   constexpr int LOADS = KT * CH / 256;    // 16-byte chunks per thread per tile (K and V each)
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * VP];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;  // MFMA row / column-in-tile and lane group
-  const int g = blockIdx.x, tile = blockIdx.y, s = blockIdx.z;
+  // the last query tiles of a chunk see the most keys: dispatch them first
+  const int g = blockIdx.x, tile = gridDim.y - 1 - blockIdx.y, s = blockIdx.z;
   const int hq = p.num_kv_heads * G;
 
   const int a = load_invariant(p.cu_q + s);
@@ -90,62 +103,82 @@ __global__ __launch_bounds__(256) void varlen_prefill_kernel(const DecodeParams 
     }
   }
 
-  float m_run[NT], l_run[NT];
+  float m_run[NT];
+  f32x4_t lacc[NT];  // every element: the row's running sum of weights
   f32x4_t oacc[NT][DT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     m_run[j] = -__builtin_inff();
-    l_run[j] = 0.f;
+    lacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[j][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+
+  // keys every row of this wave sees (0 if the wave has rows past the chunk): tiles below
+  // this bound need no mask
+  const int tok_first = i0 + (wave * NT * 16) / G;
+  const int tok_last = i0 + (wave * NT * 16 + NT * 16 - 1) / G;
+  const int wave_lim_min = tok_last >= n ? 0 : (causal ? min(L, L - n + tok_first + 1) : L);
+  const uint4 kOnes = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 x8
 
   const int* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.key_cache);
   const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.value_cache);
 
   const int ntiles = (kv_end + KT - 1) / KT;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // ---- stage the K tile (row-major) and the V tile (transposed) in LDS ------------------
-    uint4 kreg[LOADS], vreg[LOADS];
+  // Tile kt+1 is fetched into registers while tile kt is multiplied; K and V chunks are taken
+  // in row order (coalesced loads, one 16-byte LDS store each).
+  uint4 kreg[LOADS], vreg[LOADS];
+  auto fetch = [&](int kt) {
+    // the tile's 4 cache blocks: one wave-uniform (scalar) table read each
+    int ph[KT / 16];
+#pragma unroll
+    for (int b = 0; b < KT / 16; ++b) {
+      const int lb = kt * (KT / 16) + b;
+      const int e = lb * 16 < kv_end ? load_invariant(table + lb) : -1;
+      ph[b] = (e >= 0 && e < p.num_blocks) ? e : -1;
+    }
+    auto chunk = [&](const uint16_t* base, int key, int c) -> uint4 {
+      const int kidx = kt * KT + key;
+      int phys = ph[0];
+#pragma unroll
+      for (int b = 1; b < KT / 16; ++b) phys = (key >> 4) == b ? ph[b] : phys;
+      const bool ok = kidx < kv_end && phys >= 0;
+      const size_t off = (((size_t)(ok ? phys : 0) * p.num_kv_heads + g) * 16 + (kidx & 15)) * D + (size_t)c * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(base + off);
+      return ok ? v : make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN: zero them
+    };
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int q = tid + 256 * u;
-      const int key = q / CH, c = q % CH;
-      const int kidx = kt * KT + key;
-      bool ok = kidx < kv_end;
-      int phys = ok ? load_invariant(table + kidx / 16) : 0;
-      ok = ok && phys >= 0 && phys < p.num_blocks;
-      phys = ok ? phys : 0;
-      const size_t off = (((size_t)phys * p.num_kv_heads + g) * 16 + (kidx & 15)) * D + (size_t)c * 8;
-      const uint4 kv = *reinterpret_cast<const uint4*>(kc + off);
-      const uint4 vv = *reinterpret_cast<const uint4*>(vc + off);
-      kreg[u] = ok ? kv : make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN: zero them
-      vreg[u] = ok ? vv : make_uint4(0, 0, 0, 0);
+      kreg[u] = chunk(kc, q / CH, q % CH);
+      vreg[u] = chunk(vc, q / CH, q % CH);
     }
+  };
+  if (ntiles > 0) fetch(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();  // the previous tile has been consumed
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int q = tid + 256 * u;
       const int key = q / CH, c = q % CH;
       *reinterpret_cast<uint4*>(Ks + key * KP + c * 8) = kreg[u];
-      const uint32_t w[4] = {vreg[u].x, vreg[u].y, vreg[u].z, vreg[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(c * 8 + 2 * e) * VP + key] = (uint16_t)(w[e] & 0xFFFFu);
-        Vt[(c * 8 + 2 * e + 1) * VP + key] = (uint16_t)(w[e] >> 16);
-      }
+      *reinterpret_cast<uint4*>(Vs + key * VP + c * 8) = vreg[u];
     }
     __syncthreads();
+    if (kt + 1 < ntiles) fetch(kt + 1);
 
     // ---- S^T = K Q^T for the tile's 4 groups of 16 keys ------------------------------------
+    // k-step outermost: 4*NT independent accumulators between dependent MFMAs
     f32x4_t sacc[NT][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int j = 0; j < NT; ++j) sacc[j][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
         const uint4 ka = *reinterpret_cast<const uint4*>(Ks + (m * 16 + lr) * KP + 32 * kk + 8 * lg);
 #pragma unroll
         for (int j = 0; j < NT; ++j) sacc[j][m] = mfma_16x16x32(ka, qb[j][kk], sacc[j][m]);
@@ -153,56 +186,69 @@ __global__ __launch_bounds__(256) void varlen_prefill_kernel(const DecodeParams 
     }
 
     // ---- mask, online softmax (threshold rescale), P in the B-operand key order -----------
+    // Masking is needed only where a row's visible range ends inside the tile.
+    const bool whole = kt * KT + KT <= wave_lim_min;
     uint4 pb[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       float sv[4][4];
       float mx = -__builtin_inff();
+      if (whole) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt * KT + m * 16 + 4 * lg + i;
-          sv[m][i] = key < lim[j] ? sacc[j][m][i] * p.scale_log2 : -__builtin_inff();
-          mx = fmaxf(mx, sv[m][i]);
-        }
+          for (int i = 0; i < 4; ++i) {
+            sv[m][i] = sacc[j][m][i];
+            mx = fmaxf(mx, sv[m][i]);
+          }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt * KT + m * 16 + 4 * lg + i;
+            sv[m][i] = key < lim[j] ? sacc[j][m][i] : -__builtin_inff();
+            mx = fmaxf(mx, sv[m][i]);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx *= p.scale_log2;  // scale > 0: the max of the scaled scores
       const bool need = mx > m_run[j] + kTauPrefill;
       if (__any(need)) {
         const float mn = need ? mx : m_run[j];
         const float alpha = need ? fast_exp2(m_run[j] - mn) : 1.f;
-        l_run[j] *= alpha;
+        lacc[j] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[j][dt] *= alpha;
         m_run[j] = mn;
       }
+      const float mneg = m_run[j] == -__builtin_inff() ? 0.f : -m_run[j];
       uint32_t pk[4][2];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        float pv[4];
+        __bf16 b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pv[i] = sv[m][i] == -__builtin_inff() ? 0.f : fast_exp2(sv[m][i] - m_run[j]);
-        const uint32_t b0 = f32_to_bf16_rne(pv[0]), b1 = f32_to_bf16_rne(pv[1]);
-        const uint32_t b2 = f32_to_bf16_rne(pv[2]), b3 = f32_to_bf16_rne(pv[3]);
-        // the denominator sums the same rounded weights the numerator uses
-        l_run[j] += bf16lo(b0) + bf16lo(b1) + bf16lo(b2) + bf16lo(b3);
-        pk[m][0] = b0 | (b1 << 16);
-        pk[m][1] = b2 | (b3 << 16);
+        for (int i = 0; i < 4; ++i) b[i] = (__bf16)fast_exp2(fmaf(sv[m][i], p.scale_log2, mneg));  // -inf -> 0
+        pk[m][0] = (uint32_t)__builtin_bit_cast(uint16_t, b[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, b[1]) << 16);
+        pk[m][1] = (uint32_t)__builtin_bit_cast(uint16_t, b[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, b[3]) << 16);
       }
       pb[j][0] = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);  // keys 4lg.. , 16+4lg..
       pb[j][1] = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);  // keys 32+4lg.., 48+4lg..
+      // row sums of the same rounded weights, on the matrix core: ones . P^T
+      lacc[j] = mfma_16x16x32(kOnes, pb[j][0], lacc[j]);
+      lacc[j] = mfma_16x16x32(kOnes, pb[j][1], lacc[j]);
     }
 
     // ---- O^T += V^T P^T --------------------------------------------------------------------
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint16_t* vrow = Vt + (dt * 16 + lr) * VP + ks * 32 + 4 * lg;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-        const uint4 va = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      for (int dt = 0; dt < DT; ++dt) {
+        // lane lr of group lg reads dims dt*16 + 4(lr%4).. of key ks*32 + 4lg + lr/4 (and +16)
+        const uint16_t* vsrc = Vs + (ks * 32 + 4 * lg + (lr >> 2)) * VP + dt * 16 + 4 * (lr & 3);
+        const uint2 l2 = lds_read_tr16(vsrc), h2 = lds_read_tr16(vsrc + 16 * VP);
+        const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);  // V[keys sigma][dim dt*16 + lr]
 #pragma unroll
         for (int j = 0; j < NT; ++j) oacc[j][dt] = mfma_16x16x32(va, pb[j][ks], oacc[j][dt]);
       }
@@ -212,9 +258,7 @@ __global__ __launch_bounds__(256) void varlen_prefill_kernel(const DecodeParams 
   // ---- normalise and store: lane l holds dims dt*16 + 4*lg .. +3 of row l%16 --------------
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    float lt = l_run[j];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lacc[j][0];
     const int r = wave * (NT * 16) + j * 16 + lr;
     if (tok[j] >= n) continue;
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
