@@ -458,12 +458,16 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
 
 }
 
-// Merge the partitions of every (sequence, query head) that was split.
+// Merge the partitions of every (sequence, query head) that was split: M = max_j m_j,
+// w_j = 2^(m_j - M) l_j, out = sum_j w_j o_j / sum_j w_j.  256 threads: four groups of 64
+// lanes take every fourth partition (each lane D/64 dims), then combine through LDS.
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p) {
   constexpr int PER = D / 64;
+  constexpr int NG = 4;
   const int h = blockIdx.x, s = blockIdx.y;
   const int hq = gridDim.x;
+  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
   int qrow = s;
   if (p.cu_q != nullptr) {
     const int a = load_invariant(p.cu_q + s), b = load_invariant(p.cu_q + s + 1);
@@ -477,27 +481,44 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const DecodeParams p)
   const int nparts = (L + p.partition_tokens - 1) / p.partition_tokens;
   if (nparts <= 1) return;
   const size_t base = ((size_t)s * hq + h) * p.max_parts;
+  __shared__ float sm_red[NG];
+  __shared__ float sm_num[NG][D];
+
   float mx = -__builtin_inff();
-  for (int j = 0; j < nparts; ++j) mx = fmaxf(mx, p.ws_m[base + j]);
+  for (int j = threadIdx.x; j < nparts; j += 64 * NG) mx = fmaxf(mx, p.ws_m[base + j]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) sm_red[grp] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
+
   float den = 0.f;
   float num[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) num[e] = 0.f;
-  for (int j = 0; j < nparts; ++j) {
+  for (int j = grp; j < nparts; j += NG) {
     const float mj = p.ws_m[base + j];
     const float w = (mj == -__builtin_inff()) ? 0.f : fast_exp2(mj - mx) * p.ws_l[base + j];
     den += w;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = fmaf(w, p.ws_o[(base + j) * D + threadIdx.x + 64 * e], num[e]);
+    for (int e = 0; e < PER; ++e) num[e] = fmaf(w, p.ws_o[(base + j) * D + lane + 64 * e], num[e]);
   }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) sm_num[grp][lane + 64 * e] = num[e];
+  __syncthreads();  // sm_red is read above by every thread before it is rewritten here
+  if (lane == 0) sm_red[grp] = den;
+  __syncthreads();
+  if (grp != 0) return;
+  den = sm_red[0] + sm_red[1] + sm_red[2] + sm_red[3];
   const size_t orow = ((size_t)qrow * hq + h) * D;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
-    const float o = den > 0.f ? num[e] / den : 0.f;
+    const int d = lane + 64 * e;
+    const float o = den > 0.f ? (sm_num[0][d] + sm_num[1][d] + sm_num[2][d] + sm_num[3][d]) / den : 0.f;
     if constexpr (OUT_BF16)
-      reinterpret_cast<uint16_t*>(p.out)[orow + threadIdx.x + 64 * e] = (uint16_t)f32_to_bf16_rne(o);
+      reinterpret_cast<uint16_t*>(p.out)[orow + d] = (uint16_t)f32_to_bf16_rne(o);
     else
-      reinterpret_cast<float*>(p.out)[orow + threadIdx.x + 64 * e] = o;
+      reinterpret_cast<float*>(p.out)[orow + d] = o;
   }
 }
 
@@ -559,11 +580,11 @@ hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_d
   if (p.max_parts <= 1) return hipSuccess;
   dim3 grid(num_q_heads, num_seqs);
   if (head_dim == 128) {
-    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<128, true>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((decode_reduce_kernel<128, false>), grid, dim3(64), 0, stream, p);
+    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_reduce_kernel<128, false>), grid, dim3(256), 0, stream, p);
   } else if (head_dim == 64) {
-    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<64, true>), grid, dim3(64), 0, stream, p);
-    else hipLaunchKernelGGL((decode_reduce_kernel<64, false>), grid, dim3(64), 0, stream, p);
+    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<64, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_reduce_kernel<64, false>), grid, dim3(256), 0, stream, p);
   } else {
     return hipErrorInvalidValue;
   }
