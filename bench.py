@@ -263,7 +263,7 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config]),
             "avg_launch_us": round(dec_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": int(dec_bytes),
         },
