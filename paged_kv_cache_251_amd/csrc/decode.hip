@@ -24,6 +24,8 @@
 //    widen exactly to f16).
 //  * Rows, then waves, are merged at the end; a single partition writes the output,
 //    several write (o/l, m, l) to the workspace for the reduce kernel.
+#include <atomic>
+
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -79,11 +81,15 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = lane >> 4, col = lane & 15;
-  const int g = blockIdx.x, part = blockIdx.y;
+  int g = blockIdx.x;
+  const int part = blockIdx.y;
   const int hq = p.num_kv_heads * G;
   int s = blockIdx.z;
   if (p.longest_first) {
-    // rank of sequence t = #{t' : L[t'] > L[t] or (L[t'] == L[t] and t' < t)}; invert it
+    // rank of sequence t = #{t' : L[t'] > L[t] or (L[t'] == L[t] and t' < t)}; invert it.
+    // Work unit j (sequence of rank j / Hkv, KV head j % Hkv) goes to work-group
+    // i = blockIdx.z * Hkv + blockIdx.x, or, in snake order, to the mirror position of i
+    // on every second lap of p.snake work-groups.
     __shared__ int sm_len[kMaxRankedSeqs];
     __shared__ int sm_order[kMaxRankedSeqs];
     const int n = gridDim.z;
@@ -99,7 +105,14 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       sm_order[r] = t;
     }
     __syncthreads();
-    s = sm_order[blockIdx.z];
+    int j = blockIdx.z * gridDim.x + blockIdx.x;
+    if (p.snake > 0) {
+      const int lap = j / p.snake, pos = j % p.snake;
+      const int lap_len = min(p.snake, n * (int)gridDim.x - lap * p.snake);
+      if (lap & 1) j = lap * p.snake + (lap_len - 1 - pos);
+    }
+    s = sm_order[j / gridDim.x];
+    g = j % gridDim.x;
   }
 
   int qrow = s;
@@ -523,16 +536,44 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p
 }
 
 // ---------------------------------------------------------------------------------------
-// Waves per work-group of the partition kernel.  A whole-context pass (one work-group per
-// (KV head, sequence)) runs 8 waves, so one work-group fills a CU and, with the
-// longest-first order, the dispatcher hands out the remaining shorter contexts to whichever
-// CU frees up first.  A split pass has many short work-groups: 4 waves each.
+// Waves per work-group of the partition kernel: 4.  In a whole-context pass (one
+// work-group per (KV head, sequence)) a CU holds two or more work-groups, so one that ends
+// leaves the CU streaming for the others while the dispatcher refills it.  When the whole
+// grid is resident at once, the snake order balances the sum of context lengths per CU;
+// otherwise the plain longest-first order lets the dispatcher place the remaining, shorter
+// contexts on whichever CU frees up first.
 #ifndef PA_DECODE_WAVES_WHOLE
-#define PA_DECODE_WAVES_WHOLE 8
+#define PA_DECODE_WAVES_WHOLE 4
 #endif
 #ifndef PA_DECODE_WAVES_SPLIT
 #define PA_DECODE_WAVES_SPLIT 4
 #endif
+
+// CUs of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Work-groups of `kernel` (block of `threads`) that one CU holds at once (cached per kernel).
+template <typename K>
+static int resident_per_cu(K kernel, int threads) {
+  static std::atomic<int> cache{0};
+  int c = cache.load(std::memory_order_relaxed);
+  if (c > 0) return c;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, kernel, threads, 0) != hipSuccess || c <= 0) return 0;
+  cache.store(c, std::memory_order_relaxed);
+  return c;
+}
 
 template <int KV, int D, int G>
 static hipError_t launch_parts_kv_d_g(const DecodeParams& p, int num_seqs, hipStream_t stream) {
@@ -541,7 +582,15 @@ static hipError_t launch_parts_kv_d_g(const DecodeParams& p, int num_seqs, hipSt
   dim3 grid(p.num_kv_heads, p.max_parts, num_seqs);
   if (p.max_parts <= 1) {
     constexpr int W = PA_DECODE_WAVES_WHOLE;
-    hipLaunchKernelGGL((decode_partition_kernel<KV, D, G, W>), grid, dim3(64 * W), 0, stream, p);
+    auto kernel = decode_partition_kernel<KV, D, G, W>;
+    DecodeParams q = p;
+    q.snake = 0;
+    if (p.longest_first) {
+      const long long units = (long long)num_seqs * p.num_kv_heads;
+      const int cus = device_cus();
+      if (cus > 0 && units <= (long long)cus * resident_per_cu(kernel, 64 * W)) q.snake = cus;
+    }
+    hipLaunchKernelGGL(kernel, grid, dim3(64 * W), 0, stream, q);
   } else {
     constexpr int W = PA_DECODE_WAVES_SPLIT;
     hipLaunchKernelGGL((decode_partition_kernel<KV, D, G, W>), grid, dim3(64 * W), 0, stream, p);

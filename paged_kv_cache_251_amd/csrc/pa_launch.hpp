@@ -38,6 +38,11 @@ struct DecodeParams {
   // the sequences by context length (ties by index) and takes the one with its rank, so
   // the dispatcher hands out long contexts first (greedy longest-processing-time).
   int32_t longest_first;
+  // With longest_first, when every work-group of the grid is resident at once (the launcher
+  // checks the occupancy): the number of CUs.  Work-groups i and i + snake share a CU, so
+  // rank order is reversed on every second lap of this length, pairing long contexts with
+  // short ones on each CU.  0: plain rank order.
+  int32_t snake;
   int32_t causal;  // packed (varlen) batches: mask aligned to the end of each context
 };
 

@@ -108,6 +108,22 @@ def test_llama3_8b_bf16_decode_full_size():
         print(f"config 2 partition {part}: max abs err {err:.2e}")
 
 
+@pytest.mark.parametrize("dtype,hkv,n", [("bf16", 3, 100), ("e5m2", 5, 230), ("bf16", 8, 40)])
+def test_longest_first_order_covers_every_sequence_and_head(dtype, hkv, n):
+    """Whole-context pass with more (sequence, KV head) units than CUs, a count that is not a
+    multiple of the CU count, and many equal lengths: every unit is attended exactly once
+    (the longest-first and snake orders only decide which work-group takes which unit)."""
+    rng = np.random.default_rng(n)
+    lens = rng.integers(0, 300, size=n)
+    lens[::7] = 64  # ties
+    w = make_workload(lens, num_q_heads=hkv * 2, num_kv_heads=hkv, head_dim=64, q_dtype="bf16",
+                      kv_dtype=dtype, seed=n)
+    b = DeviceBatch(w)
+    pk, pv = oracle_pools(w)
+    ref = _oracle_decode(w, pk, pv)
+    assert_close(out_f64(b.decode(0), "bf16"), ref, "bf16", f"{dtype} {n}x{hkv} whole-context")
+
+
 def _perm_pools(w, b: DeviceBatch, seed=5):
     rng = np.random.default_rng(seed)
     perm = rng.permutation(w.num_blocks)
