@@ -398,7 +398,7 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
   p.causal = causal;
   hipError_t e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
   if (e == hipSuccess) e = pa::launch_decode_reduce(p, true, head_dim, num_kv_heads * gqa_group, num_seqs, stream);
-  if (e == hipSuccess) e = pa::launch_varlen_prefill(p, head_dim, gqa_group, num_seqs, max_q_len, stream);
+  if (e == hipSuccess) e = pa::launch_varlen_prefill(p, head_dim, gqa_group, num_seqs, total_q, max_q_len, stream);
   return device_status(e, fn);
 }
 

@@ -44,6 +44,9 @@ struct DecodeParams {
   // short ones on each CU.  0: plain rank order.
   int32_t snake;
   int32_t causal;  // packed (varlen) batches: mask aligned to the end of each context
+  // Prefill kernel: number of sequences to rank into the longest-first unit order (the grid
+  // is then one-dimensional); 0: natural three-dimensional order.
+  int32_t sched_seqs;
 };
 
 // Partition pass: a sequence with one partition gets its output row; a split one gets
@@ -55,8 +58,8 @@ hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_d
                                 hipStream_t stream);
 
 // Prefill rows (sequences with >= 2 query tokens) of a packed batch, on MFMA.
-hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
-                                 hipStream_t stream);
+hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int total_q,
+                                 int max_q_len, hipStream_t stream);
 
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* cu, const int32_t* end_pos,
                                const int32_t* tables, int32_t max_blocks, int32_t num_seqs,

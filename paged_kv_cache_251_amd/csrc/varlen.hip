@@ -24,6 +24,15 @@
 // result is element i%4 of the 8 bytes read by lane 4j + i/4.  So if lane k of the group reads
 // dims 4(k%4)..+3 of key k/4, lane i receives dim i of the 4 keys -- a column of V.
 // Every accumulator of lane l belongs to row l%16: the online-softmax rescale is per lane.
+//
+// Order of work: a work unit is (sequence, 128-row query tile, KV head); the causal mask makes
+// its cost proportional to the keys it sees, kv_end.  For batches of up to kMaxScheduledSeqs
+// sequences the grid is one-dimensional and work-group j takes the unit of rank j / Hkv in
+// descending kv_end over every sequence (head j % Hkv), so the dispatcher hands out the
+// longest units first across all chunks, and the grid's spare work-groups come last.
+#include <algorithm>
+#include <climits>
+
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -34,6 +43,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr float kTauPrefill = 8.0f;
+constexpr int kMaxScheduledSeqs = 1024;
 
 // ds_read_b64_tr_b16 on an LDS address (see the lane mapping above)
 __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
@@ -65,19 +75,119 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;  // MFMA row / column-in-tile and lane group
-  // the last query tiles of a chunk see the most keys: dispatch them first
-  const int g = blockIdx.x, tile = gridDim.y - 1 - blockIdx.y, s = blockIdx.z;
   const int hq = p.num_kv_heads * G;
+  auto clamp_len = [&](int L) {
+    L = L < 0 ? 0 : L;
+    L = L > p.max_context_len ? p.max_context_len : L;
+    return L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
+  };
+
+  int g, tile, s;
+  if (p.sched_seqs > 0) {
+    // ---- longest-first schedule -------------------------------------------------------------
+    // Sequences with n >= 2 query tokens, compacted by wave 0: base = L - n, n.  Tile t of such
+    // a sequence has the sort key L - n + min(n, (t+1)*TOKW), strictly increasing in t (ties
+    // between sequences: lower compacted index first).
+    __shared__ int sm_base[kMaxScheduledSeqs], sm_n[kMaxScheduledSeqs], sm_seq[kMaxScheduledSeqs];
+    __shared__ int sm_count;
+    const int nseq = p.sched_seqs;
+    if (wave == 0) {
+      int cnt = 0;
+      for (int s0 = 0; s0 < nseq; s0 += 64) {
+        const int si = s0 + lane;
+        int nn = 0, base = 0;
+        if (si < nseq) {
+          nn = p.cu_q[si + 1] - p.cu_q[si];
+          base = clamp_len(p.context_lens[si]) - nn;
+        }
+        const bool take = si < nseq && nn >= 2;
+        const uint64_t bal = __ballot(take);
+        const int pos = cnt + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (take) {
+          sm_base[pos] = base;
+          sm_n[pos] = nn;
+          sm_seq[pos] = si;
+        }
+        cnt += __builtin_popcountll(bal);
+      }
+      if (lane == 0) sm_count = cnt;
+    }
+    __syncthreads();
+    const int M = __builtin_amdgcn_readfirstlane(sm_count);
+    const int pair = blockIdx.x / p.num_kv_heads;
+    g = blockIdx.x % p.num_kv_heads;
+    // number of tiles whose key exceeds K (every wave computes it; the result is wave-uniform)
+    auto count_gt = [&](int K) {
+      int c = 0;
+      for (int m = lane; m < M; m += 64) {
+        const int x = K - sm_base[m], nn = sm_n[m];
+        const int T = (nn + TOKW - 1) / TOKW;
+        c += x < 0 ? T : (x >= nn ? 0 : T - x / TOKW);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+      return __builtin_amdgcn_readfirstlane(c);
+    };
+    int klo = INT_MAX, khi = INT_MIN;
+    for (int m = lane; m < M; m += 64) {
+      klo = min(klo, sm_base[m] + 1);
+      khi = max(khi, sm_base[m] + sm_n[m]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      klo = min(klo, __shfl_xor(klo, off));
+      khi = max(khi, __shfl_xor(khi, off));
+    }
+    klo = __builtin_amdgcn_readfirstlane(klo);
+    khi = __builtin_amdgcn_readfirstlane(khi);
+    if (M == 0 || pair >= count_gt(klo - 1)) return;  // spare work-group
+    // the key of the unit of rank `pair`: the largest K with more than `pair` keys >= K
+    while (klo < khi) {
+      const int mid = klo + (int)(((long long)khi - klo + 1) / 2);
+      if (count_gt(mid - 1) > pair) klo = mid;
+      else khi = mid - 1;
+    }
+    const int rank_in_key = pair - count_gt(klo);  // among the tiles whose key equals klo
+    s = -1;
+    tile = 0;
+    int seen = 0;
+    for (int m0 = 0; m0 < M; m0 += 64) {
+      const int m = m0 + lane;
+      bool has = false;
+      int tt = 0;
+      if (m < M) {
+        const int x = klo - sm_base[m], nn = sm_n[m];
+        has = x == nn || (x >= TOKW && x < nn && x % TOKW == 0);
+        tt = x == nn ? (nn + TOKW - 1) / TOKW - 1 : x / TOKW - 1;
+      }
+      const uint64_t bal = __ballot(has);
+      const int c = __builtin_popcountll(bal);
+      if (rank_in_key < seen + c) {
+        const bool me = has && __builtin_popcountll(bal & ((1ull << lane) - 1ull)) == rank_in_key - seen;
+        const int src = __builtin_ctzll(__ballot(me));
+        s = __shfl(m < M ? sm_seq[m] : 0, src);
+        tile = __shfl(tt, src);
+        break;
+      }
+      seen += c;
+    }
+    // wave-uniform from here on (every lane took the same branch of the search)
+    s = __builtin_amdgcn_readfirstlane(s);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    if (s < 0) return;  // not reached: every rank below the unit count has a unit
+  } else {
+    // natural order, the last query tiles of a chunk (the most keys) first
+    g = blockIdx.x;
+    tile = gridDim.y - 1 - blockIdx.y;
+    s = blockIdx.z;
+  }
 
   const int a = load_invariant(p.cu_q + s);
   const int n = load_invariant(p.cu_q + s + 1) - a;
   if (n <= 1) return;  // decode rows: the decode kernel
   const int i0 = tile * TOKW;
   if (i0 >= n) return;
-  int L = load_invariant(p.context_lens + s);
-  L = L < 0 ? 0 : L;
-  L = L > p.max_context_len ? p.max_context_len : L;
-  L = L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
+  const int L = clamp_len(load_invariant(p.context_lens + s));
   const bool causal = p.causal != 0;
   // keys any row of this work-group may see
   const int last_tok = min(n, i0 + TOKW) - 1;
@@ -129,14 +239,49 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
   // Tile kt+1 is fetched into registers while tile kt is multiplied; K and V chunks are taken
   // in row order (coalesced loads, one 16-byte LDS store each).
   uint4 kreg[LOADS], vreg[LOADS];
-  auto fetch = [&](int kt) {
-    // the tile's 4 cache blocks: one wave-uniform (scalar) table read each
+  // Chunk u of this thread is 16-byte piece tid % CH of key tid / CH + u * (256 / CH) of the
+  // tile; those keys lie in cache block u * (256 / CH) / 16 + (tid / CH) / 16 of the tile,
+  // the same block for the whole wave, at a fixed offset inside the block.
+  const uint32_t lane_off = ((uint32_t)(g * 16 + (tid / CH) % 16)) * D + (uint32_t)(tid % CH) * 8;
+  const int wave_blk = __builtin_amdgcn_readfirstlane((tid / CH) / 16);
+  const size_t blk_stride = (size_t)p.num_kv_heads * 16 * D;
+  // The 4 cache blocks of a tile: one wave-uniform (scalar) table read each, issued one tile
+  // ahead of the loads that use them.
+  struct TileBlocks {
     int ph[KT / 16];
+  };
+  auto read_table = [&](int kt) {
+    TileBlocks t;
 #pragma unroll
     for (int b = 0; b < KT / 16; ++b) {
       const int lb = kt * (KT / 16) + b;
-      const int e = lb * 16 < kv_end ? load_invariant(table + lb) : -1;
-      ph[b] = (e >= 0 && e < p.num_blocks) ? e : -1;
+      t.ph[b] = lb * 16 < kv_end ? load_invariant(table + lb) : -1;
+    }
+    return t;
+  };
+  auto fetch = [&](int kt, const TileBlocks& t) {
+    int ph[KT / 16];
+    bool all_valid = kt * KT + KT <= kv_end;
+#pragma unroll
+    for (int b = 0; b < KT / 16; ++b) {
+      const int e = t.ph[b];
+      const bool v = e >= 0 && e < p.num_blocks;
+      all_valid = all_valid && v;
+      ph[b] = v ? e : -1;
+    }
+    if (all_valid) {  // every key of the tile is visible to some row and stored: no checks
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int blk = u * (256 / CH) / 16 + wave_blk;
+        int phys = ph[0];
+#pragma unroll
+        for (int b = 1; b < KT / 16; ++b) phys = blk == b ? ph[b] : phys;
+        const uint16_t* kb = kc + (size_t)phys * blk_stride;
+        const uint16_t* vb = vc + (size_t)phys * blk_stride;
+        kreg[u] = *reinterpret_cast<const uint4*>(kb + lane_off);
+        vreg[u] = *reinterpret_cast<const uint4*>(vb + lane_off);
+      }
+      return;
     }
     auto chunk = [&](const uint16_t* base, int key, int c) -> uint4 {
       const int kidx = kt * KT + key;
@@ -155,7 +300,9 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
       vreg[u] = chunk(vc, q / CH, q % CH);
     }
   };
-  if (ntiles > 0) fetch(0);
+  TileBlocks tb_next{};
+  if (ntiles > 0) fetch(0, read_table(0));
+  if (ntiles > 1) tb_next = read_table(1);
   for (int kt = 0; kt < ntiles; ++kt) {
     __syncthreads();  // the previous tile has been consumed
 #pragma unroll
@@ -166,7 +313,10 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
       *reinterpret_cast<uint4*>(Vs + key * VP + c * 8) = vreg[u];
     }
     __syncthreads();
-    if (kt + 1 < ntiles) fetch(kt + 1);
+    if (kt + 1 < ntiles) {
+      fetch(kt + 1, tb_next);
+      if (kt + 2 < ntiles) tb_next = read_table(kt + 2);
+    }
 
     // ---- S^T = K Q^T for the tile's 4 groups of 16 keys ------------------------------------
     // k-step outermost: 4*NT independent accumulators between dependent MFMAs
@@ -211,11 +361,13 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
             mx = fmaxf(mx, sv[m][i]);
           }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      mx *= p.scale_log2;  // scale > 0: the max of the scaled scores
-      const bool need = mx > m_run[j] + kTauPrefill;
-      if (__any(need)) {
+      // The row's running max only moves when some score exceeds it by more than the
+      // threshold; the lanes' own maxima decide whether the row maxima are needed at all.
+      if (__any(mx * p.scale_log2 > m_run[j] + kTauPrefill)) {  // scale > 0
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx *= p.scale_log2;
+        const bool need = mx > m_run[j] + kTauPrefill;
         const float mn = need ? mx : m_run[j];
         const float alpha = need ? fast_exp2(m_run[j] - mn) : 1.f;
         lacc[j] *= alpha;
@@ -273,30 +425,45 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
 }
 
 template <int D, int G>
-static hipError_t launch_prefill_dg(const DecodeParams& p, int num_seqs, int max_q_len, hipStream_t stream) {
+static hipError_t launch_prefill_dg(const DecodeParams& p, int num_seqs, int total_q, int max_q_len,
+                                   hipStream_t stream) {
   constexpr int TOKW = 128 / G;
-  dim3 grid(p.num_kv_heads, (max_q_len + TOKW - 1) / TOKW, num_seqs);
-  hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), grid, dim3(256), 0, stream, p);
+  DecodeParams q = p;
+  const long long tiles_per_seq = (max_q_len + TOKW - 1) / TOKW;
+  if (num_seqs <= kMaxScheduledSeqs) {
+    // At most min(N, total_q / 2) sequences have n >= 2, and together they hold at most
+    // total_q tokens, so they have at most (total_q + that count * (TOKW - 1)) / TOKW tiles.
+    const long long chunks = std::min<long long>(num_seqs, total_q / 2);
+    const long long units = std::min<long long>((total_q + chunks * (TOKW - 1)) / TOKW, tiles_per_seq * num_seqs);
+    q.sched_seqs = num_seqs;
+    hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), dim3((unsigned)(units * p.num_kv_heads)), dim3(256), 0,
+                       stream, q);
+  } else {
+    q.sched_seqs = 0;
+    dim3 grid(p.num_kv_heads, (unsigned)tiles_per_seq, num_seqs);
+    hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), grid, dim3(256), 0, stream, q);
+  }
   return hipGetLastError();
 }
 
 template <int D>
-static hipError_t launch_prefill_d(const DecodeParams& p, int gqa, int num_seqs, int max_q_len, hipStream_t stream) {
+static hipError_t launch_prefill_d(const DecodeParams& p, int gqa, int num_seqs, int total_q, int max_q_len,
+                                   hipStream_t stream) {
   switch (gqa) {
-    case 1: return launch_prefill_dg<D, 1>(p, num_seqs, max_q_len, stream);
-    case 2: return launch_prefill_dg<D, 2>(p, num_seqs, max_q_len, stream);
-    case 4: return launch_prefill_dg<D, 4>(p, num_seqs, max_q_len, stream);
-    case 8: return launch_prefill_dg<D, 8>(p, num_seqs, max_q_len, stream);
-    case 16: return launch_prefill_dg<D, 16>(p, num_seqs, max_q_len, stream);
+    case 1: return launch_prefill_dg<D, 1>(p, num_seqs, total_q, max_q_len, stream);
+    case 2: return launch_prefill_dg<D, 2>(p, num_seqs, total_q, max_q_len, stream);
+    case 4: return launch_prefill_dg<D, 4>(p, num_seqs, total_q, max_q_len, stream);
+    case 8: return launch_prefill_dg<D, 8>(p, num_seqs, total_q, max_q_len, stream);
+    case 16: return launch_prefill_dg<D, 16>(p, num_seqs, total_q, max_q_len, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
-                                 hipStream_t stream) {
+hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int total_q,
+                                 int max_q_len, hipStream_t stream) {
   if (max_q_len <= 1) return hipSuccess;  // no sequence has two or more query tokens
-  if (head_dim == 128) return launch_prefill_d<128>(p, gqa, num_seqs, max_q_len, stream);
-  if (head_dim == 64) return launch_prefill_d<64>(p, gqa, num_seqs, max_q_len, stream);
+  if (head_dim == 128) return launch_prefill_d<128>(p, gqa, num_seqs, total_q, max_q_len, stream);
+  if (head_dim == 64) return launch_prefill_d<64>(p, gqa, num_seqs, total_q, max_q_len, stream);
   return hipErrorInvalidValue;
 }
 

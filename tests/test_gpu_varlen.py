@@ -65,6 +65,18 @@ def test_varlen_edge_lengths(G, D, causal):
         assert_close(out_f64(_varlen(b, part, causal), "bf16"), ref, "bf16", f"varlen G{G} D{D} causal {causal}")
 
 
+def test_varlen_more_sequences_than_the_ranked_limit():
+    """Over 1024 sequences: both kernels fall back to their natural work order."""
+    rng = np.random.default_rng(77)
+    n_new = np.ones(1030, np.int64)
+    n_new[[3, 500, 1029, 17, 800]] = [2, 33, 70, 5, 128]
+    lens = n_new + rng.integers(0, 64, size=1030)
+    w = make_workload(lens, q_lens=n_new, num_q_heads=4, num_kv_heads=2, head_dim=64, q_dtype="bf16", seed=77)
+    b = DeviceBatch(w)
+    pk, pv = oracle_pools(w)
+    assert_close(out_f64(_varlen(b, 0), "bf16"), _oracle_rows(w, pk, pv), "bf16", "1030 sequences")
+
+
 def test_varlen_block_permutation_and_packing_order_are_bit_identical():
     w = _mixed(5, 4, 128)
     b = DeviceBatch(w)
