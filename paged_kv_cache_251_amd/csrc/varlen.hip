@@ -69,8 +69,10 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
   constexpr int VP = D + 16;              // V row pitch in LDS: 4 rows x 4 chunks hit distinct banks
   constexpr int CH = D / 8;               // 16-byte chunks per K/V row
   constexpr int LOADS = KT * CH / 256;    // 16-byte chunks per thread per tile (K and V each)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * VP];
+  // two K and two V tiles (double buffer); the schedule's arrays use the same memory first
+  constexpr int KBUF = KT * KP, VBUF = KT * VP;
+  static_assert((2 * KBUF + 2 * VBUF) * 2 >= (3 * kMaxScheduledSeqs + 1) * 4, "schedule arrays fit in the tiles");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * KBUF + 2 * VBUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -88,8 +90,10 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
     // Sequences with n >= 2 query tokens, compacted by wave 0: base = L - n, n.  Tile t of such
     // a sequence has the sort key L - n + min(n, (t+1)*TOKW), strictly increasing in t (ties
     // between sequences: lower compacted index first).
-    __shared__ int sm_base[kMaxScheduledSeqs], sm_n[kMaxScheduledSeqs], sm_seq[kMaxScheduledSeqs];
-    __shared__ int sm_count;
+    int* sm_base = reinterpret_cast<int*>(lds);
+    int* sm_n = sm_base + kMaxScheduledSeqs;
+    int* sm_seq = sm_n + kMaxScheduledSeqs;
+    int* sm_count = sm_seq + kMaxScheduledSeqs;
     const int nseq = p.sched_seqs;
     if (wave == 0) {
       int cnt = 0;
@@ -110,10 +114,10 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
         }
         cnt += __builtin_popcountll(bal);
       }
-      if (lane == 0) sm_count = cnt;
+      if (lane == 0) *sm_count = cnt;
     }
     __syncthreads();
-    const int M = __builtin_amdgcn_readfirstlane(sm_count);
+    const int M = __builtin_amdgcn_readfirstlane(*sm_count);
     const int pair = blockIdx.x / p.num_kv_heads;
     g = blockIdx.x % p.num_kv_heads;
     // number of tiles whose key exceeds K (every wave computes it; the result is wave-uniform)
@@ -175,6 +179,7 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
     s = __builtin_amdgcn_readfirstlane(s);
     tile = __builtin_amdgcn_readfirstlane(tile);
     if (s < 0) return;  // not reached: every rank below the unit count has a unit
+    __syncthreads();    // the schedule's arrays are done with before the tiles reuse them
   } else {
     // natural order, the last query tiles of a chunk (the most keys) first
     g = blockIdx.x;
@@ -269,13 +274,13 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
       all_valid = all_valid && v;
       ph[b] = v ? e : -1;
     }
+    // block of chunk u: BPU * u + wave_blk (compile-time indices only, so ph stays in SGPRs)
+    constexpr int BPU = (256 / CH) / 16;
+    auto block_of = [&](int u) { return BPU == 1 ? ph[u] : (wave_blk ? ph[BPU * u + 1] : ph[BPU * u]); };
     if (all_valid) {  // every key of the tile is visible to some row and stored: no checks
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
-        const int blk = u * (256 / CH) / 16 + wave_blk;
-        int phys = ph[0];
-#pragma unroll
-        for (int b = 1; b < KT / 16; ++b) phys = blk == b ? ph[b] : phys;
+        const int phys = block_of(u);
         const uint16_t* kb = kc + (size_t)phys * blk_stride;
         const uint16_t* vb = vc + (size_t)phys * blk_stride;
         kreg[u] = *reinterpret_cast<const uint4*>(kb + lane_off);
@@ -283,41 +288,47 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
       }
       return;
     }
-    auto chunk = [&](const uint16_t* base, int key, int c) -> uint4 {
-      const int kidx = kt * KT + key;
-      int phys = ph[0];
-#pragma unroll
-      for (int b = 1; b < KT / 16; ++b) phys = (key >> 4) == b ? ph[b] : phys;
-      const bool ok = kidx < kv_end && phys >= 0;
-      const size_t off = (((size_t)(ok ? phys : 0) * p.num_kv_heads + g) * 16 + (kidx & 15)) * D + (size_t)c * 8;
-      const uint4 v = *reinterpret_cast<const uint4*>(base + off);
-      return ok ? v : make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN: zero them
-    };
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int q = tid + 256 * u;
-      kreg[u] = chunk(kc, q / CH, q % CH);
-      vreg[u] = chunk(vc, q / CH, q % CH);
+      const int phys = block_of(u);
+      const int kidx = kt * KT + (tid + 256 * u) / CH;
+      const bool ok = kidx < kv_end && phys >= 0;
+      const uint16_t* kb = kc + (size_t)(ok ? phys : 0) * blk_stride;
+      const uint16_t* vb = vc + (size_t)(ok ? phys : 0) * blk_stride;
+      const uint4 kv4 = *reinterpret_cast<const uint4*>(kb + lane_off);
+      const uint4 vv4 = *reinterpret_cast<const uint4*>(vb + lane_off);
+      kreg[u] = ok ? kv4 : make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN: zero them
+      vreg[u] = ok ? vv4 : make_uint4(0, 0, 0, 0);
     }
   };
-  TileBlocks tb_next{};
-  if (ntiles > 0) fetch(0, read_table(0));
-  if (ntiles > 1) tb_next = read_table(1);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();  // the previous tile has been consumed
+  // Tile kt is multiplied out of buffer kt % 2 while tile kt + 1 waits in registers; after
+  // the multiply it goes to the other buffer (free since the previous barrier) and the loads
+  // of tile kt + 2 are issued: one barrier per tile.
+  auto store = [&](int buf) {
+    uint16_t* kd = lds + buf * KBUF;
+    uint16_t* vd = lds + 2 * KBUF + buf * VBUF;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int q = tid + 256 * u;
       const int key = q / CH, c = q % CH;
-      *reinterpret_cast<uint4*>(Ks + key * KP + c * 8) = kreg[u];
-      *reinterpret_cast<uint4*>(Vs + key * VP + c * 8) = vreg[u];
+      *reinterpret_cast<uint4*>(kd + key * KP + c * 8) = kreg[u];
+      *reinterpret_cast<uint4*>(vd + key * VP + c * 8) = vreg[u];
+    }
+  };
+  TileBlocks tb_next{};
+  if (ntiles > 0) {
+    fetch(0, read_table(0));
+    if (ntiles > 1) tb_next = read_table(1);
+    store(0);
+    if (ntiles > 1) {
+      fetch(1, tb_next);
+      if (ntiles > 2) tb_next = read_table(2);
     }
     __syncthreads();
-    if (kt + 1 < ntiles) {
-      fetch(kt + 1, tb_next);
-      if (kt + 2 < ntiles) tb_next = read_table(kt + 2);
-    }
-
+  }
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const uint16_t* Ks = lds + (kt & 1) * KBUF;
+    const uint16_t* Vs = lds + 2 * KBUF + (kt & 1) * VBUF;
     // ---- S^T = K Q^T for the tile's 4 groups of 16 keys ------------------------------------
     // k-step outermost: 4*NT independent accumulators between dependent MFMAs
     f32x4_t sacc[NT][4];
@@ -405,6 +416,14 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
         for (int j = 0; j < NT; ++j) oacc[j][dt] = mfma_16x16x32(va, pb[j][ks], oacc[j][dt]);
       }
     }
+    if (kt + 1 < ntiles) {
+      store((kt + 1) & 1);
+      if (kt + 2 < ntiles) {
+        fetch(kt + 2, tb_next);
+        if (kt + 3 < ntiles) tb_next = read_table(kt + 3);
+      }
+    }
+    __syncthreads();
   }
 
   // ---- normalise and store: lane l holds dims dt*16 + 4*lg .. +3 of row l%16 --------------
