@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload 1-5 (1-4 decode, 5 packed prefill + decode)")
+    ap.add_argument("--config", type=int, default=2, help="workload 1-6 (1-4 decode, 5 packed prefill + decode, 6 speculative verification of 4 tokens)")
     ap.add_argument("--replicas", type=int, default=0, help="resident batches to rotate (0: enough for >= 1.2 GB)")
     ap.add_argument("--partition", type=int, default=None, help="partition tokens (default: workload's, else auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
@@ -171,8 +171,8 @@ class VarlenBatch:
 
         self._keep = []
         self.args_varlen = varlen_args(0, n)
-        self.args_prefill_only = varlen_args(0, n_pre)
-        self.args_decode_only = varlen_args(n_pre, n)
+        self.args_prefill_only = varlen_args(0, n_pre) if n_pre > 0 else None
+        self.args_decode_only = varlen_args(n_pre, n) if n_pre < n else None
         self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * d * 2 * 2
         self.decode_kv_bytes = int(w.context_lens[n_pre:].astype("int64").sum()) * hkv * d * 2 * 2
         pos = [(int(L) - int(qn) + i + 1) for L, qn in zip(w.context_lens[:n_pre], w.q_lens[:n_pre]) for i in range(qn)]
@@ -216,6 +216,9 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
 
     dec = lambda b: check(lib.paged_attention_varlen(*b.args_decode_only, sh), "varlen decode rows")
     pre = lambda b: check(lib.paged_attention_varlen(*b.args_prefill_only, sh), "varlen prefill rows")
+    if batches[0].args_decode_only is None:  # every sequence verifies several tokens
+        bench_multi_token(args, batches, timed, pre, step, np)
+        return
     _, dec_ms = timed(dec, True)
     _, pre_ms = timed(pre, True)
     ms_step, _ = timed(step, False)
@@ -276,6 +279,67 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
             "frac": round(pre_tflops / 2500.0, 4),
             "avg_call_us": round(pre_ms * 1e3, 3),
             "flops_per_call": int(pre_flops),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_multi_token(args, batches, timed, call, step, np):
+    """A batch whose every sequence attends several new tokens (speculative verification): one
+    kernel streams each (sequence, KV head) context once for all its query rows, so the roofline is
+    HBM on the same algorithmic KV bytes as a decode step."""
+    from workloads import CONFIG_NAMES
+
+    w0 = batches[0].w
+    reps = len(batches)
+    _, call_ms = timed(call, True)
+    ms_step, _ = timed(step, False)
+    step_bytes = float(np.mean([batches[i % reps].kv_bytes for i in range(args.steps)]))
+    flops = float(np.mean([batches[i % reps].prefill_flops for i in range(args.steps)]))
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    call_gbs = step_bytes / (call_ms * 1e-3) / 1e9
+    cpu = None if args.no_cpu_baseline else cpu_baseline_varlen(w0, args.cpu_seconds)
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": CONFIG_NAMES[args.config],
+            "num_seqs": w0.num_seqs,
+            "tokens_per_seq": int(w0.max_q_len),
+            "num_q_heads": w0.num_q_heads,
+            "num_kv_heads": w0.num_kv_heads,
+            "head_dim": w0.head_dim,
+            "block_size": w0.block_size,
+            "resident_batches": reps,
+            "step": "slot mapping + cache write of every new token + paged_attention_varlen (causal among "
+                    "the new tokens)",
+        },
+        "seq_steps_per_s": round(w0.num_seqs / (ms_step * 1e-3), 1),
+        "tokens_per_s": round(w0.total_q / (ms_step * 1e-3), 1),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "kv_bytes_per_step": int(step_bytes),
+        "roofline": {
+            "kernel": "varlen_prefill_kernel (every row; no decode launch)",
+            "bound": "hbm",
+            "achieved": round(call_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(call_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config]),
+            "avg_launch_us": round(call_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": int(step_bytes),
+            "mfma_tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
         },
         "cpu_baseline": cpu,
     }

@@ -396,9 +396,20 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
   if (prefill_tiles > kMaxGridYZ) return fail(PA_ERR_UNSUPPORTED, "%s: max_q_len %d too large", fn, max_q_len);
   p.cu_q = cu_seqlens_q;
   p.causal = causal;
-  hipError_t e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
-  if (e == hipSuccess) e = pa::launch_decode_reduce(p, true, head_dim, num_kv_heads * gqa_group, num_seqs, stream);
-  if (e == hipSuccess) e = pa::launch_varlen_prefill(p, head_dim, gqa_group, num_seqs, total_q, max_q_len, stream);
+  // Every sequence holds at most max_q_len of the total_q rows, so when total_q equals
+  // num_seqs * max_q_len >= 2 * num_seqs none has a single row: no decode launch.
+  const bool single_rows = !(max_q_len >= 2 && static_cast<int64_t>(total_q) == static_cast<int64_t>(num_seqs) * max_q_len);
+  hipError_t e = hipSuccess;
+  if (single_rows) {
+    e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
+    if (e == hipSuccess) e = pa::launch_decode_reduce(p, true, head_dim, num_kv_heads * gqa_group, num_seqs, stream);
+  }
+  if (e == hipSuccess) {
+    if (pa::multiquery_applies(gqa_group, max_q_len))
+      e = pa::launch_varlen_multiquery(p, head_dim, gqa_group, num_seqs, max_q_len, stream);
+    else
+      e = pa::launch_varlen_prefill(p, head_dim, gqa_group, num_seqs, total_q, max_q_len, stream);
+  }
   return device_status(e, fn);
 }
 

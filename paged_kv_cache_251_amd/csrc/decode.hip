@@ -86,33 +86,11 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   const int hq = p.num_kv_heads * G;
   int s = blockIdx.z;
   if (p.longest_first) {
-    // rank of sequence t = #{t' : L[t'] > L[t] or (L[t'] == L[t] and t' < t)}; invert it.
-    // Work unit j (sequence of rank j / Hkv, KV head j % Hkv) goes to work-group
-    // i = blockIdx.z * Hkv + blockIdx.x, or, in snake order, to the mirror position of i
-    // on every second lap of p.snake work-groups.
     __shared__ int sm_len[kMaxRankedSeqs];
     __shared__ int sm_order[kMaxRankedSeqs];
-    const int n = gridDim.z;
-    for (int t = threadIdx.x; t < n; t += 64 * W) sm_len[t] = load_invariant(p.context_lens + t);
-    __syncthreads();
-    for (int t = threadIdx.x; t < n; t += 64 * W) {
-      const int lt = sm_len[t];
-      int r = 0;
-      for (int u = 0; u < n; ++u) {
-        const int lu = sm_len[u];
-        r += (lu > lt) | ((lu == lt) & (u < t));
-      }
-      sm_order[r] = t;
-    }
-    __syncthreads();
-    int j = blockIdx.z * gridDim.x + blockIdx.x;
-    if (p.snake > 0) {
-      const int lap = j / p.snake, pos = j % p.snake;
-      const int lap_len = min(p.snake, n * (int)gridDim.x - lap * p.snake);
-      if (lap & 1) j = lap * p.snake + (lap_len - 1 - pos);
-    }
-    s = sm_order[j / gridDim.x];
-    g = j % gridDim.x;
+    const int2 u = longest_first_unit<64 * W>(p.context_lens, gridDim.z, gridDim.x, p.snake, sm_len, sm_order);
+    s = u.x;
+    g = u.y;
   }
 
   int qrow = s;

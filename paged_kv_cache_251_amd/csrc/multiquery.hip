@@ -1,0 +1,339 @@
+// Multi-token decode of a packed (varlen) step on gfx950 MFMA: sequences that attend a few new
+// tokens at once, n * G <= 16 * NT query rows per KV head (speculative verification of draft
+// tokens, short prefill chunks).
+//
+// Same attention as the prefill tiles (Colossal-Inference release post, "连续批量化算法
+// (Continuous Batching)": packed 1-D rows; LLM inference optimisation overview, 2.2.2 "GQA"
+// and 2.2.1 "Flash Attention": the G heads of a group share the K/V, softmax reduced block by
+// block), but shaped like decode: with few query rows the cost is streaming each (sequence,
+// KV head) context once, so one work-group takes one context and its 4 waves split the
+// context's 16-key cache blocks (block b goes to wave b % 4), merging through LDS at the end.
+//
+// Per block and 16-row tile, with lane l, lg = l / 16:
+//   S^T[16 keys][16 rows] = K . Q^T       v_mfma_f32_16x16x32_bf16 x (D / 32); A = K straight
+//                                          from global memory (lane l: key l % 16, dims
+//                                          32 kk + 8 lg ..), B = Q from registers
+//   O^T[D][16 rows]      += V^T . P^T     v_mfma_f32_16x16x16_bf16 x (D / 16); B = P^T is the
+//                                          S^T accumulator itself (lane l: keys 4 lg .. 4 lg + 3
+//                                          of row l % 16, rounded to bf16), A = V^T read from
+//                                          the wave's own row-major copy of the block in LDS with
+//                                          ds_read_b64_tr_b16
+// Row sums come from the same rounded weights through an MFMA with a ones matrix.
+#include <atomic>
+
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+
+namespace pa {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 mq_bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float mq_f32x4_t;
+typedef short mq_v4i16_t __attribute__((ext_vector_type(4)));
+
+constexpr float kTauMq = 8.0f;
+constexpr int kMaxRankedMq = 1024;
+
+__device__ __forceinline__ mq_f32x4_t mfma_k32(const uint4& a, const uint4& b, const mq_f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8_t, a), __builtin_bit_cast(mq_bf16x8_t, b),
+                                                 c, 0, 0, 0);
+}
+__device__ __forceinline__ mq_f32x4_t mfma_k16(const uint2& a, const uint2& b, const mq_f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mq_v4i16_t, a), __builtin_bit_cast(mq_v4i16_t, b),
+                                                   c, 0, 0, 0);
+}
+// ds_read_b64_tr_b16: within each 16-lane group, lane i's j-th 16-bit result is element i % 4 of
+// the 8 bytes read by lane 4 j + i / 4 (checked on the device)
+__device__ __forceinline__ uint2 mq_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) mq_v4i16_t lds_v4i16_t;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p)));
+}
+
+}  // namespace
+
+template <int D, int G, int NT>
+__global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeParams p) {
+  constexpr int W = 4;
+  constexpr int ROWS = NT * 16;       // query rows of the work-group: row r = (token r / G, head r % G)
+  constexpr int KS = D / 32;          // k-steps of the QK product
+  constexpr int DT = D / 16;          // 16-dim output tiles
+  constexpr int CH = D / 8;           // 16-byte chunks per cache row
+  constexpr int VP = D + 16;          // row pitch of a wave's V copy (bf16): conflict-free transposed reads
+  constexpr int VLD = 16 * CH / 64;   // 16-byte V chunks per lane per block
+  constexpr int VWAVE = 16 * VP;      // bf16 per wave's V copy
+  constexpr int MERGE = W * ROWS * (D + 2);  // floats: each wave's o, m, l
+  constexpr int LDS_BYTES = (MERGE * 4 > W * VWAVE * 2 + 2 * kMaxRankedMq * 4) ? MERGE * 4
+                                                                               : W * VWAVE * 2 + 2 * kMaxRankedMq * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int hq = p.num_kv_heads * G;
+
+  int s = blockIdx.z, g = blockIdx.x;
+  if (p.longest_first) {
+    int* len = reinterpret_cast<int*>(lds + W * VWAVE * 2);
+    const int2 u = longest_first_unit<64 * W>(p.context_lens, gridDim.z, gridDim.x, p.snake, len, len + kMaxRankedMq);
+    s = u.x;
+    g = u.y;
+  }
+  const int a = load_invariant(p.cu_q + s);
+  const int n = load_invariant(p.cu_q + s + 1) - a;
+  if (n <= 1) return;  // single rows: the decode kernel
+  int L = load_invariant(p.context_lens + s);
+  L = L < 0 ? 0 : L;
+  L = L > p.max_context_len ? p.max_context_len : L;
+  L = L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
+  const bool causal = p.causal != 0;
+
+  // ---- query rows (B operand of S^T = K Q^T) ----------------------------------------------
+  int tok[NT], lim[NT];
+  uint4 qb[NT][KS];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int r = j * 16 + lr;
+    tok[j] = r / G;
+    const bool ok = tok[j] < n;
+    lim[j] = ok ? (causal ? min(L, L - n + tok[j] + 1) : L) : 0;  // keys [0, lim) visible
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(p.query) + ((size_t)(a + (ok ? tok[j] : 0)) * hq + (size_t)g * G + r % G) * D;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg);
+      qb[j][kk] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+  // the keys every valid row of the work-group sees: blocks below need no mask
+  const int last_tok = min(n, ROWS / G) - 1;
+  const int lim_min = causal ? min(L, L - n + 1) : L;  // token 0
+  const int kv_end = max(0, causal ? min(L, L - n + last_tok + 1) : L);
+
+  float m_run[NT];
+  mq_f32x4_t lacc[NT], oacc[NT][DT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    m_run[j] = -__builtin_inff();
+    lacc[j] = mq_f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[j][dt] = mq_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const uint2 kOnes = make_uint2(0x3F803F80u, 0x3F803F80u);  // bf16 1.0 x4
+
+  const int* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.key_cache);
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.value_cache);
+  const size_t blk_bytes = (size_t)p.num_kv_heads * 16 * D * 2;
+  const uint32_t k_off = (uint32_t)(((g * 16 + lr) * D + 8 * lg) * 2);  // + 64 kk bytes
+  uint32_t v_off[VLD];
+  int v_lds[VLD];
+#pragma unroll
+  for (int u = 0; u < VLD; ++u) {
+    const int q = lane + 64 * u, key = q / CH, c = q % CH;
+    v_off[u] = (uint32_t)(((g * 16 + key) * D + c * 8) * 2);
+    v_lds[u] = key * VP + c * 8;
+  }
+  uint16_t* vs = reinterpret_cast<uint16_t*>(lds) + wave * VWAVE;
+  // lane m of group lg reads key 4 lg + m / 4, dims dt * 16 + 4 (m % 4): V^T for dims dt*16 + lr
+  const int v_rd = (4 * lg + (lr >> 2)) * VP + 4 * (lr & 3);
+
+  struct Block {
+    uint4 k[KS];
+    uint4 v[VLD];
+    bool ok;
+  };
+  auto load_block = [&](int b, Block& t) {
+    int phys = load_invariant(table + b);
+    t.ok = phys >= 0 && phys < p.num_blocks;
+    phys = t.ok ? phys : 0;
+    const uint8_t* kb = kc + (size_t)phys * blk_bytes;
+    const uint8_t* vb = vc + (size_t)phys * blk_bytes;
+    auto ld16 = [](const uint8_t* q) {
+      const u32x4_t v = ld<u32x4_t, true>(q);  // streamed once
+      return make_uint4(v.x, v.y, v.z, v.w);
+    };
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) t.k[kk] = ld16(kb + k_off + 64 * kk);
+#pragma unroll
+    for (int u = 0; u < VLD; ++u) t.v[u] = ld16(vb + v_off[u]);
+    __builtin_amdgcn_sched_barrier(0);  // issue the block before the math that follows
+  };
+
+  auto compute_block = [&](int b, Block& t) {
+    // the wave's V copy: rows past the context are zeroed (the pool may hold NaN there)
+    const int live = t.ok ? min(16, kv_end - 16 * b) : 0;
+#pragma unroll
+    for (int u = 0; u < VLD; ++u) {
+      const int key = (lane + 64 * u) / CH;
+      *reinterpret_cast<uint4*>(vs + v_lds[u]) = key < live ? t.v[u] : make_uint4(0, 0, 0, 0);
+    }
+    const bool whole = t.ok && 16 * b + 16 <= lim_min;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      mq_f32x4_t sa = mq_f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) sa = mfma_k32(t.k[kk], qb[j][kk], sa);
+      float sv[4];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * b + 4 * lg + i;
+        sv[i] = (whole || (t.ok && key < lim[j])) ? sa[i] : -__builtin_inff();
+        mx = fmaxf(mx, sv[i]);
+      }
+      // the row's running max moves only past the threshold; lanes' own maxima gate the reduction
+      if (__any(mx * p.scale_log2 > m_run[j] + kTauMq)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx *= p.scale_log2;
+        const bool need = mx > m_run[j] + kTauMq;
+        const float mn = need ? mx : m_run[j];
+        const float alpha = need ? fast_exp2(m_run[j] - mn) : 1.f;
+        lacc[j] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[j][dt] *= alpha;
+        m_run[j] = mn;
+      }
+      const float mneg = m_run[j] == -__builtin_inff() ? 0.f : -m_run[j];
+      __bf16 pb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = (__bf16)fast_exp2(fmaf(sv[i], p.scale_log2, mneg));  // -inf -> 0
+      const uint2 pt = make_uint2(
+          (uint32_t)__builtin_bit_cast(uint16_t, pb[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, pb[1]) << 16),
+          (uint32_t)__builtin_bit_cast(uint16_t, pb[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, pb[3]) << 16));
+      lacc[j] = mfma_k16(kOnes, pt, lacc[j]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint2 va = mq_read_tr16(vs + v_rd + dt * 16);  // V^T[dims dt*16 + lr][keys 4lg..]
+        oacc[j][dt] = mfma_k16(va, pt, oacc[j][dt]);
+      }
+    }
+  };
+
+  // ---- stream the context: block b on wave b % W, one block of prefetch -----------------
+  const int nblk = (kv_end + 15) / 16;
+  const int nb = wave < nblk ? (nblk - wave + W - 1) / W : 0;
+  if (nb > 0) {
+    Block x, y;
+    int b = wave;
+    load_block(b, x);
+    int i = 0;
+    for (; i + 2 < nb; i += 2) {
+      load_block(b + W, y);
+      compute_block(b, x);
+      load_block(b + 2 * W, x);
+      compute_block(b + W, y);
+      b += 2 * W;
+    }
+    if (i + 1 < nb) {
+      load_block(b + W, y);
+      compute_block(b, x);
+      compute_block(b + W, y);
+    } else {
+      compute_block(b, x);
+    }
+  }
+
+  // ---- merge the waves: o (unnormalised), m, l per row through LDS ------------------------
+  __syncthreads();  // the V copies are done with
+  float* mo = reinterpret_cast<float*>(lds);          // [W][ROWS][D]
+  float* mm = mo + W * ROWS * D;                       // [W][ROWS]
+  float* ml = mm + W * ROWS;                           // [W][ROWS]
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int r = j * 16 + lr;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mo[(wave * ROWS + r) * D + dt * 16 + 4 * lg + i] = oacc[j][dt][i];
+    if (lg == 0) {
+      mm[wave * ROWS + r] = m_run[j];
+      ml[wave * ROWS + r] = lacc[j][0];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ROWS * D; idx += 64 * W) {
+    const int r = idx / D, d = idx % D;
+    const int t = r / G;
+    if (t >= n) continue;
+    float mx = mm[r];
+#pragma unroll
+    for (int w = 1; w < W; ++w) mx = fmaxf(mx, mm[w * ROWS + r]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = mm[w * ROWS + r];
+      const float c = mw == -__builtin_inff() ? 0.f : fast_exp2(mw - mx);
+      num = fmaf(c, mo[(w * ROWS + r) * D + d], num);
+      den = fmaf(c, ml[w * ROWS + r], den);
+    }
+    const float o = den > 0.f ? num / den : 0.f;
+    reinterpret_cast<uint16_t*>(p.out)[((size_t)(a + t) * hq + (size_t)g * G + r % G) * D + d] =
+        (uint16_t)f32_to_bf16_rne(o);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+namespace {
+
+int mq_device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && (cus = cache[dev].load(std::memory_order_relaxed)) > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+template <int D, int G, int NT>
+hipError_t launch_mq_dgn(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+  auto kernel = varlen_multiquery_kernel<D, G, NT>;
+  DecodeParams q = p;
+  q.longest_first = num_seqs <= kMaxRankedMq ? 1 : 0;
+  q.snake = 0;
+  if (q.longest_first) {
+    // snake order when the whole grid is resident at once (as for the decode kernel)
+    static std::atomic<int> per_cu_cache{0};
+    int per_cu = per_cu_cache.load(std::memory_order_relaxed);
+    if (per_cu <= 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
+      per_cu_cache.store(per_cu, std::memory_order_relaxed);
+    const int cus = mq_device_cus();
+    if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu) q.snake = cus;
+  }
+  hipLaunchKernelGGL(kernel, dim3(p.num_kv_heads, 1, num_seqs), dim3(256), 0, stream, q);
+  return hipGetLastError();
+}
+
+template <int D, int G>
+hipError_t launch_mq_dg(const DecodeParams& p, int num_seqs, int max_q_len, hipStream_t stream) {
+  if (max_q_len * G <= 16) return launch_mq_dgn<D, G, 1>(p, num_seqs, stream);
+  return launch_mq_dgn<D, G, 2>(p, num_seqs, stream);
+}
+
+template <int D>
+hipError_t launch_mq_d(const DecodeParams& p, int gqa, int num_seqs, int max_q_len, hipStream_t stream) {
+  switch (gqa) {
+    case 1: return launch_mq_dg<D, 1>(p, num_seqs, max_q_len, stream);
+    case 2: return launch_mq_dg<D, 2>(p, num_seqs, max_q_len, stream);
+    case 4: return launch_mq_dg<D, 4>(p, num_seqs, max_q_len, stream);
+    case 8: return launch_mq_dg<D, 8>(p, num_seqs, max_q_len, stream);
+    case 16: return launch_mq_dg<D, 16>(p, num_seqs, max_q_len, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool multiquery_applies(int gqa, int max_q_len) { return max_q_len >= 2 && max_q_len * gqa <= 32; }
+
+hipError_t launch_varlen_multiquery(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
+                                    hipStream_t stream) {
+  if (!multiquery_applies(gqa, max_q_len)) return hipErrorInvalidValue;
+  if (head_dim == 128) return launch_mq_d<128>(p, gqa, num_seqs, max_q_len, stream);
+  if (head_dim == 64) return launch_mq_d<64>(p, gqa, num_seqs, max_q_len, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

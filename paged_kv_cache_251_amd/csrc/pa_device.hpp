@@ -229,4 +229,35 @@ __device__ __forceinline__ T load_invariant(const T* p) {
       reinterpret_cast<const __attribute__((address_space(4))) char*>(reinterpret_cast<uintptr_t>(p)));
 }
 
+// Longest-first work order over (sequence, KV head) units.  Ranks the n sequences by context
+// length (rank of t = #{t' : L[t'] > L[t] or (L[t'] == L[t] and t' < t)}) in LDS (`len`,
+// `order`: n ints each, n <= their size) and returns the unit of work-group
+// j = blockIdx.z * hkv + blockIdx.x: sequence of rank j / hkv, KV head j % hkv.  With snake > 0
+// (every work-group of the grid resident at once; work-groups i and i + snake share a CU) the
+// order is mirrored on every second lap of `snake` work-groups, pairing long and short contexts
+// on each CU.  Every thread of the work-group must call it (it synchronises).
+template <int THREADS>
+__device__ __forceinline__ int2 longest_first_unit(const int32_t* context_lens, int n, int hkv, int snake,
+                                                   int* len, int* order) {
+  for (int t = threadIdx.x; t < n; t += THREADS) len[t] = load_invariant(context_lens + t);
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += THREADS) {
+    const int lt = len[t];
+    int r = 0;
+    for (int u = 0; u < n; ++u) {
+      const int lu = len[u];
+      r += (lu > lt) | ((lu == lt) & (u < t));
+    }
+    order[r] = t;
+  }
+  __syncthreads();
+  int j = blockIdx.z * hkv + blockIdx.x;
+  if (snake > 0) {
+    const int lap = j / snake, pos = j % snake;
+    const int lap_len = min(snake, n * hkv - lap * snake);
+    if (lap & 1) j = lap * snake + (lap_len - 1 - pos);
+  }
+  return make_int2(order[j / hkv], j % hkv);
+}
+
 }  // namespace pa

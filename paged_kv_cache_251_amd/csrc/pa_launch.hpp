@@ -57,6 +57,12 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
                                 hipStream_t stream);
 
+// Multi-token rows of a packed batch when every sequence has at most max_q_len tokens and
+// max_q_len * gqa <= 32 (speculative verification): one work-group streams each context once.
+bool multiquery_applies(int gqa, int max_q_len);
+hipError_t launch_varlen_multiquery(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
+                                    hipStream_t stream);
+
 // Prefill rows (sequences with >= 2 query tokens) of a packed batch, on MFMA.
 hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int total_q,
                                  int max_q_len, hipStream_t stream);

@@ -100,7 +100,10 @@ def out_f64(t: torch.Tensor, dtype: str) -> np.ndarray:
 
 def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
     """The parity bar: fp32 within 1e-5 of each output row's largest magnitude
-    (normwise, per (row, head)); bf16 and e5m2-cache results within 1e-2 absolute."""
+    (normwise, per (row, head)); bf16 outputs (bf16 or e5m2 cache) within 1e-2 absolute on top
+    of the output format's own rounding.  A bf16 number has 8 significant bits, so even the
+    correctly rounded exact result can sit 2^-8 |ref| away from it (0.0156 at |ref| = 4, when a
+    short context averages a few large values); that much is added to the 1e-2 elementwise."""
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     if dtype == "f32":
@@ -109,6 +112,9 @@ def assert_close(got: np.ndarray, ref: np.ndarray, dtype: str, what: str = ""):
         bad = err > bound
         assert not bad.any(), f"{what}: fp32 row error {err[bad].max():.3e} over bound {bound[bad].min():.3e}"
     else:
-        err = np.abs(got - ref).max()
-        assert err <= 1e-2, f"{what}: max abs error {err:.3e} > 1e-2"
+        diff = np.abs(got - ref)
+        bound = 1e-2 + 2.0**-8 * np.abs(ref)
+        bad = diff > bound
+        assert not bad.any(), (f"{what}: abs error {diff[bad].max():.3e} over its bound "
+                               f"(1e-2 + 2^-8 |ref|, |ref| = {np.abs(ref)[bad][np.argmax(diff[bad])]:.3f})")
     return float(np.abs(got - ref).max())

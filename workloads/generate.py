@@ -33,6 +33,7 @@ CONFIG_NAMES = {
     3: "llama3_8b_decode_e5m2_kv",
     4: "long_context_split_kv_bf16",
     5: "varlen_prefill_decode_bf16",
+    6: "llama3_8b_spec_verify_k4_bf16",
 }
 
 # random streams
@@ -258,6 +259,12 @@ def make_config(idx: int, replica: int = 0) -> Workload:
         return make_workload(lens, q_lens=qlens, num_q_heads=32, num_kv_heads=8, head_dim=128,
                              q_dtype="bf16", shared_seqs=shared, shared_prefix_blocks=prefix_blocks,
                              causal=True, seed=seed, name=name)
+    if idx == 6:
+        # speculative verification: every sequence of the Llama-3-8B decode batch checks 4 draft
+        # tokens at once (causal among them, the context counting them)
+        lens = rl.integers(512, 2048 + 1, size=64)
+        return make_workload(lens, q_lens=np.full(64, 4), num_q_heads=32, num_kv_heads=8, head_dim=128,
+                             q_dtype="bf16", causal=True, seed=seed, name=name)
     raise ValueError(f"no workload {idx}")
 
 
