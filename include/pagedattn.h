@@ -260,8 +260,12 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
  *   other arguments as in paged_attention_decode; the workspace is sized by
  *   paged_attention_workspace_size(num_seqs, ...) and serves the 1-token rows.
  * Rows with n_s = 1 go through the decode kernels (split-KV when partition_size asks for
- * it); rows of sequences with n_s >= 2 through MFMA tiles.  Supported: bf16 query and cache.
- * A row whose position is negative (n_s > L) sees no key and comes out zero.
+ * it); rows of sequences with n_s >= 2 through MFMA: when max_q_len * gqa_group <= 32 (a few
+ * tokens per sequence, e.g. draft tokens of speculative decoding) one pass over each context
+ * serves all its rows, otherwise 128-row query tiles.  When total_q = num_seqs * max_q_len and
+ * max_q_len >= 2 no sequence has a single row and the decode kernel is not launched.
+ * Supported: bf16 query and cache.  A row whose position is negative (n_s > L) sees no key and
+ * comes out zero.
  */
 pa_status_t paged_attention_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
                                    const int32_t* cu_seqlens_q, const int32_t* context_lens,
