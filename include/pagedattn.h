@@ -7,6 +7,8 @@
  *         "分页注意力算法 (PagedAttention)", "连续批量化算法 (Continuous Batching)".
  *   [OPT] LLM inference optimisation overview ("AI 大模型推理优化技术详解"),
  *         sections 2.1.2 "Paged Attention", 2.2.1 "Flash Attention", 2.2.2 "GQA".
+ *   [TACO] Taco-LLM article ("易用性对齐 vLLM，推理效率提升超200%，这款国产加速框架什么来头？"),
+ *         section "使用 Prefix Cache 技术降低 TTFT".
  *
  * Data model
  *   Every sequence's keys and values live in fixed-size blocks of `block_size`
@@ -60,14 +62,15 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARGUMENT = 1,
   PA_ERR_UNSUPPORTED = 2,
   PA_ERR_WORKSPACE_TOO_SMALL = 3,
-  PA_ERR_DEVICE = 4
+  PA_ERR_DEVICE = 4,
+  PA_ERR_OUT_OF_BLOCKS = 5
 } pa_status_t;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E5M2 = 2 } pa_dtype_t;
@@ -275,6 +278,90 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
                                    float scale, int32_t causal, pa_dtype_t q_dtype, pa_dtype_t kv_dtype,
                                    int32_t partition_size, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------------------
+ * Block manager (host side): which physical blocks of the pool each sequence owns.
+ * [CI BlockedKeyValueCache: blocks are taken from the pool as tokens arrive, and only a
+ *  sequence's last block is partly empty; OPT 2.1.2: a pool of blocks reserved up front, a
+ *  table from logical to physical blocks, several logical blocks may name one physical block,
+ *  a block in use has a reference count of one or more and is freed when it drops to zero;
+ *  TACO Prefix Cache: the cache of earlier prompts is kept as a prefix tree, and the matching
+ *  part of a new prompt is read from it instead of being computed]
+ *
+ * Rules (the pages fix the reference counting; the rest is this library's choice):
+ *   - A new block is the lowest-numbered free block.
+ *   - A sequence given its token ids registers each block it fills completely in the prefix
+ *     tree, keyed by (parent block, the block's block_size token ids); the first block's
+ *     parent is "none".  The caller must write a registered block's K/V before any later call
+ *     can hand the block to another sequence (in one serving step: write, then schedule).
+ *   - pa_bm_add_sequence with token ids reuses the longest chain of registered blocks that
+ *     matches the prompt, up to (num_tokens - 1) / block_size blocks so that at least one token
+ *     is left to compute; *cached_tokens tells how many leading tokens are already stored.
+ *   - A block whose count drops to zero is free again if it is not registered; a registered
+ *     one stays reusable until its block is needed: then the least recently released
+ *     registered block with no registered child is evicted (ties: deeper first, then lower id).
+ *   - Copy on write: appending to a sequence whose last, partly filled block is shared moves the
+ *     sequence to a new block and reports the copy (old -> new) for paged_kv_copy_blocks.
+ *   - Every call either succeeds or changes nothing.  PA_ERR_OUT_OF_BLOCKS: the pool (free plus
+ *     evictable blocks) cannot supply the blocks the call needs.
+ * A manager is not thread-safe; different managers may be used from different threads.
+ * ---------------------------------------------------------------------------------------
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager for a pool of num_blocks blocks of block_size tokens (both > 0). */
+pa_status_t pa_bm_create(int32_t num_blocks, int32_t block_size, pa_block_manager** manager);
+void pa_bm_destroy(pa_block_manager* manager);
+
+/*
+ * A new sequence seq_id (not in use) holding num_tokens >= 0 tokens.  token_ids (host,
+ * [num_tokens]) may be null: then the sequence takes no part in prefix reuse, and its appends
+ * must pass null too.  *cached_tokens (may be null) = leading tokens whose K/V are already in
+ * reused blocks (a multiple of block_size); the caller writes the rest.
+ */
+pa_status_t pa_bm_add_sequence(pa_block_manager* manager, int64_t seq_id, const int32_t* token_ids,
+                               int32_t num_tokens, int32_t* cached_tokens);
+
+/*
+ * Append num_tokens >= 0 tokens to seq_id (token_ids as for pa_bm_add_sequence).  When the
+ * last block is partly filled and shared, the sequence moves to a new block first and the copy
+ * is reported as copies[0] = old block, copies[1] = new block, *num_copies = 1 (0 otherwise);
+ * copies must then hold max_copies >= 1 pairs.
+ */
+pa_status_t pa_bm_append(pa_block_manager* manager, int64_t seq_id, const int32_t* token_ids, int32_t num_tokens,
+                         int32_t* copies, int32_t max_copies, int32_t* num_copies);
+
+/* child_id (not in use) shares every block of parent_id (counts + 1): a fork of the sequence. */
+pa_status_t pa_bm_fork(pa_block_manager* manager, int64_t parent_id, int64_t child_id);
+
+/* Release every block of seq_id and forget the sequence. */
+pa_status_t pa_bm_free_sequence(pa_block_manager* manager, int64_t seq_id);
+
+/*
+ * The block table of seq_id: table[0 .. *num_blocks-1] (host, max_blocks entries), and its
+ * token count.  PA_ERR_INVALID_ARGUMENT if it does not fit in max_blocks.
+ */
+pa_status_t pa_bm_block_table(const pa_block_manager* manager, int64_t seq_id, int32_t* table, int32_t max_blocks,
+                              int32_t* num_blocks, int32_t* num_tokens);
+
+/*
+ * Pool state: free (never registered or released unregistered) blocks, registered blocks
+ * (held or evictable), blocks with a count of one or more.  Any pointer may be null.
+ */
+pa_status_t pa_bm_stats(const pa_block_manager* manager, int32_t* free_blocks, int32_t* registered_blocks,
+                        int32_t* used_blocks);
+
+/*
+ * paged_kv_copy_blocks -- copy whole blocks of both pools: for i < num_pairs, block
+ * pairs[2i] -> block pairs[2i+1] (every KV head, every slot).  Carries out the copies that
+ * pa_bm_append reports.  pairs: device int32 [2 * num_pairs]; a pair with an entry outside
+ * [0, num_blocks) or src == dst is skipped; two pairs with the same destination race.
+ * cache_dtype: PA_F32, PA_BF16 or PA_FP8_E5M2 (bytes are copied).
+ */
+pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 pa_dtype_t cache_dtype, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,10 +9,12 @@ from .binding import (  # noqa: F401
     PA_BF16,
     PA_F32,
     PA_FP8_E5M2,
+    BlockManager,
     PagedAttnError,
     abi_version,
     alloc_workspace,
     auto_partition,
+    copy_blocks,
     kv_cache_write,
     lib,
     paged_attention_decode,

@@ -17,9 +17,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_F32, PA_BF16, PA_FP8_E5M2 = 0, 1, 2
-STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "device error"}
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "device error",
+          5: "out of blocks"}
+PA_ERR_OUT_OF_BLOCKS = 5
 
 _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+_i64, _pi32 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
 
 # name -> (restype, argtypes), in header order
 SIGNATURES = {
@@ -44,6 +47,15 @@ SIGNATURES = {
     "paged_attention_varlen": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _f32, _i32, ctypes.c_int, ctypes.c_int, _i32,
                                               _vp, _sz, _vp]),
+    "pa_bm_create": (ctypes.c_int, [_i32, _i32, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_add_sequence": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32]),
+    "pa_bm_append": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32, _i32, _pi32]),
+    "pa_bm_fork": (ctypes.c_int, [_vp, _i64, _i64]),
+    "pa_bm_free_sequence": (ctypes.c_int, [_vp, _i64]),
+    "pa_bm_block_table": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32, _pi32]),
+    "pa_bm_stats": (ctypes.c_int, [_vp, _pi32, _pi32, _pi32]),
+    "paged_kv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]),
 }
 PA_APPEND_SKIP_REDUCE = 1
 
@@ -260,3 +272,85 @@ def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_c
         1 if causal else 0, dtype_code(query), dtype_code(key_cache), partition_size, _ptr(workspace),
         0 if workspace is None else workspace.numel(), _stream()))
     return out
+
+
+# ------------------------------------------------------------------------------ block manager
+def _ids(tokens):
+    """Host int32 array (ctypes) of token ids, or None."""
+    if tokens is None:
+        return None, 0
+    arr = (ctypes.c_int32 * len(tokens))(*[int(t) for t in tokens])
+    return arr, len(tokens)
+
+
+class BlockManager:
+    """Host-side block manager of the library (pa_bm_*): block tables of sequences over a pool of
+    num_blocks blocks, with reference-counted sharing, copy on write and prefix reuse."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = _vp()
+        _check("pa_bm_create", lib().pa_bm_create(num_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks, self.block_size = num_blocks, block_size
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_sequence(self, seq_id: int, num_tokens: int, tokens=None) -> int:
+        """Returns the number of leading tokens already held by reused blocks."""
+        arr, n = _ids(tokens)
+        if tokens is not None:
+            _expect(n == num_tokens, "tokens must have num_tokens entries")
+        cached = ctypes.c_int32(0)
+        _check("pa_bm_add_sequence", lib().pa_bm_add_sequence(self._h, seq_id, arr, num_tokens, ctypes.byref(cached)))
+        return cached.value
+
+    def append(self, seq_id: int, num_tokens: int, tokens=None):
+        """Returns the copies [(src, dst)] the caller must carry out before writing."""
+        arr, n = _ids(tokens)
+        if tokens is not None:
+            _expect(n == num_tokens, "tokens must have num_tokens entries")
+        copies = (ctypes.c_int32 * 2)()
+        ncopies = ctypes.c_int32(0)
+        _check("pa_bm_append", lib().pa_bm_append(self._h, seq_id, arr, num_tokens, copies, 1, ctypes.byref(ncopies)))
+        return [(copies[0], copies[1])] if ncopies.value else []
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check("pa_bm_fork", lib().pa_bm_fork(self._h, parent_id, child_id))
+
+    def free_sequence(self, seq_id: int) -> None:
+        _check("pa_bm_free_sequence", lib().pa_bm_free_sequence(self._h, seq_id))
+
+    def block_table(self, seq_id: int):
+        """(list of block ids, number of tokens)."""
+        nb, nt = ctypes.c_int32(0), ctypes.c_int32(0)
+        cap = self.num_blocks
+        table = (ctypes.c_int32 * cap)()
+        _check("pa_bm_block_table", lib().pa_bm_block_table(self._h, seq_id, table, cap, ctypes.byref(nb),
+                                                            ctypes.byref(nt)))
+        return list(table[: nb.value]), nt.value
+
+    def stats(self):
+        """(free, registered, used) block counts."""
+        f, r, u = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        _check("pa_bm_stats", lib().pa_bm_stats(self._h, ctypes.byref(f), ctypes.byref(r), ctypes.byref(u)))
+        return f.value, r.value, u.value
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, pairs: torch.Tensor) -> None:
+    """Carry out block copies [(src, dst)] (int32 [n, 2] on the GPU) in both pools."""
+    _dev(key_cache, value_cache, pairs)
+    _int32(pairs)
+    _expect(key_cache.shape == value_cache.shape and key_cache.dim() == 4, "pools must be [blocks, heads, B, D]")
+    nb, hkv, bs, d = key_cache.shape
+    _check("paged_kv_copy_blocks", lib().paged_kv_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(),
+                                                               pairs.data_ptr(), pairs.numel() // 2, hkv, d, bs, nb,
+                                                               dtype_code(key_cache), _stream()))

@@ -9,8 +9,9 @@
 #include <string>
 
 #include "pa_launch.hpp"
+#include "pa_status.hpp"
 
-namespace {
+namespace pa {
 
 thread_local std::string g_last_error;
 
@@ -28,6 +29,14 @@ pa_status_t ok() {
   g_last_error.clear();
   return PA_OK;
 }
+
+}  // namespace pa
+
+namespace {
+
+using pa::fail;
+using pa::ok;
+using pa::g_last_error;
 
 pa_status_t device_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -136,6 +145,7 @@ const char* pa_status_string(pa_status_t s) {
     case PA_ERR_UNSUPPORTED: return "unsupported";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PA_ERR_DEVICE: return "device error";
+    case PA_ERR_OUT_OF_BLOCKS: return "out of blocks";
   }
   return "unknown status";
 }
@@ -411,6 +421,25 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
       e = pa::launch_varlen_prefill(p, head_dim, gqa_group, num_seqs, total_q, max_q_len, stream);
   }
   return device_status(e, fn);
+}
+
+pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 pa_dtype_t cache_dtype, hipStream_t stream) {
+  const char* fn = "paged_kv_copy_blocks";
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_pairs %d < 0", fn, num_pairs);
+  if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_kv_heads, head_dim, block_size and num_blocks must be > 0", fn);
+  if (!valid_dtype(cache_dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: unknown cache dtype %d", fn, (int)cache_dtype);
+  const size_t elem = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
+  const size_t block_bytes = static_cast<size_t>(num_kv_heads) * block_size * head_dim * elem;
+  if (block_bytes % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: a block of %zu bytes is not a multiple of 16", fn, block_bytes);
+  if (num_pairs == 0) return ok();
+  if (!key_cache || !value_cache || !pairs) return fail(PA_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(pairs, 4))
+    return fail(PA_ERR_INVALID_ARGUMENT, "%s: caches must be 16-byte aligned", fn);
+  return device_status(pa::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, block_bytes, num_blocks, stream),
+                       fn);
 }
 
 }  // extern "C"

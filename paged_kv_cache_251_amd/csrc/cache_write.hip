@@ -116,4 +116,25 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
   return hipGetLastError();
 }
 
+// Whole-block copies of both pools (copy on write of a shared, partly filled block): work-group
+// (pair, pool) copies one block of `block_bytes` with 16-byte loads and stores.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* key_cache, uint8_t* value_cache,
+                                                          const int32_t* pairs, size_t block_bytes, int32_t num_blocks) {
+  const int32_t src = pairs[2 * (size_t)blockIdx.x], dst = pairs[2 * (size_t)blockIdx.x + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+  uint8_t* base = blockIdx.y == 0 ? key_cache : value_cache;
+  const uint4* from = reinterpret_cast<const uint4*>(base + (size_t)src * block_bytes);
+  uint4* to = reinterpret_cast<uint4*>(base + (size_t)dst * block_bytes);
+  for (size_t i = threadIdx.x; i < block_bytes / 16; i += 256) to[i] = from[i];
+}
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
+                              size_t block_bytes, int32_t num_blocks, hipStream_t stream) {
+  if (num_pairs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, stream,
+                     static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache), pairs, block_bytes,
+                     num_blocks);
+  return hipGetLastError();
+}
+
 }  // namespace pa

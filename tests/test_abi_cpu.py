@@ -46,7 +46,8 @@ def test_binding_signatures_cover_the_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
+    assert lib.pa_status_string(5) == b"out of blocks"
     assert lib.pa_status_string(0) == b"ok"
     assert lib.pa_status_string(3) == b"workspace too small"
 
