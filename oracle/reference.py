@@ -7,7 +7,9 @@ Sources, cited by page title and section:
         sections "分块式KV缓存 (BlockedKeyValueCache)", "KV缓存量化 (KVCache Quant)",
         "分页注意力算法 (PagedAttention)", "连续批量化算法 (Continuous Batching)".
   [OPT] LLM inference optimisation overview ("AI 大模型推理优化技术详解"):
-        sections "2.1.2 Paged Attention", "2.2.1 Flash Attention", "2.2.2 GQA".
+        sections "2.1.2 Paged Attention", "2.2.1 Flash Attention", "2.2.2 GQA",
+        "2.6 低比特量化".
+  [FW]  LLM inference frameworks page (LMDeploy section: KV Cache INT8 quantisation).
 
 What the pages fix, restated:
   * Each sequence's keys and values are cut into blocks of a fixed number of
@@ -24,6 +26,10 @@ What the pages fix, restated:
     ``combine_partials`` state that identity for split-KV.
   * Prefill and decode tokens are processed together as one packed 1-D token
     stream without padding [CI Continuous Batching]; ``paged_varlen``.
+  * Low-bit KV caches save memory and traffic in a memory-bound step [OPT 2.6];
+    an INT8 KV cache is one such format [FW: frameworks page, LMDeploy: KV Cache
+    INT8].  No page fixes a scheme, so ``quantize_int8`` states the library's:
+    symmetric, one float32 scale per (token, KV head) row.
 
 Storage conventions: raw bits as in device memory -- f32 as float32, bf16 as
 uint16 patterns, e5m2 as uint8 codes.  The oracle's own pool layout is
@@ -90,6 +96,8 @@ def f64_to_e5m2(x) -> np.ndarray:
 
 
 def decode_storage(raw, dtype: str) -> np.ndarray:
+    if dtype == "f64":  # values already decoded (e.g. a dequantised int8 pool)
+        return np.asarray(raw, dtype=np.float64)
     if dtype == "f32":
         return np.asarray(raw, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -97,6 +105,35 @@ def decode_storage(raw, dtype: str) -> np.ndarray:
     if dtype == "e5m2":
         return e5m2_to_f64(raw)
     raise ValueError(dtype)
+
+
+# --------------------------------------------------------------------------
+# int8 rows with a scale  [OPT 2.6; FW LMDeploy KV Cache INT8; the scheme is this library's]
+# --------------------------------------------------------------------------
+def quantize_int8(x) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric int8 codes of every row (last axis) and one float32 scale per row.
+
+    All in float32 arithmetic (IEEE, round to nearest even), which fixes every
+    code bit for bit:
+        amax  = max |x|            (maxNum: a NaN element is ignored)
+        inv   = 127 / amax
+        code  = clamp(rint(x * inv), -127, 127)   (clamp by minNum/maxNum: NaN -> -127)
+        scale = amax / 127
+    A row of zeros has codes 0 and scale 0.  The dequantised value is code * scale.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        amax = np.fmax.reduce(np.abs(x32), axis=-1)
+        inv = np.where(amax > 0, np.float32(127) / amax, np.float32(0)).astype(np.float32)
+        prod = (x32 * inv[..., None]).astype(np.float32)
+        code = np.fmin(np.fmax(np.rint(prod), np.float32(-127)), np.float32(127))
+        scale = (amax / np.float32(127)).astype(np.float32)
+    return code.astype(np.int8), scale
+
+
+def dequantize_int8(codes, scales) -> np.ndarray:
+    """code * scale in float64 (exact: an 8-bit integer times a float32)."""
+    return np.asarray(codes, np.float64) * np.asarray(scales, np.float64)[..., None]
 
 
 # --------------------------------------------------------------------------
