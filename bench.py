@@ -30,7 +30,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: KV-read HBM GB/s (% of peak) + seq-steps/sec, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-KV_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1}
+KV_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1, "int8": 1}
+
+
+def row_bytes(w) -> int:
+    """Pool bytes of one (token, KV head) row: head_dim elements, plus the float32 scale of an
+    INT8 row."""
+    return w.head_dim * KV_BYTES[w.kv_dtype] + (4 if w.kv_dtype == "int8" else 0)
 
 
 def parse():
@@ -38,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload 1-6 (1-4 decode, 5 packed prefill + decode, 6 speculative verification of 4 tokens)")
+    ap.add_argument("--config", type=int, default=2, help="workload 1-7 (1-4 decode, 5 packed prefill + decode, 6 speculative verification of 4 tokens, "
+                    "7 decode over an INT8 pool)")
     ap.add_argument("--replicas", type=int, default=0, help="resident batches to rotate (0: enough for >= 1.2 GB)")
     ap.add_argument("--partition", type=int, default=None, help="partition tokens (default: workload's, else auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
@@ -75,10 +82,16 @@ class Batch:
         self.w = w
         self.tables = torch.from_numpy(w.block_tables).to(dev)
         self.lens = torch.from_numpy(w.context_lens).to(dev)
-        shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-        ints = {"f32": torch.int32, "bf16": torch.int16, "e5m2": torch.uint8}[w.kv_dtype]
-        store = {"f32": torch.float32, "bf16": torch.bfloat16, "e5m2": torch.uint8}[w.kv_dtype]
-        self.pk = torch.full(shape, POISON_BITS[w.kv_dtype], dtype=ints, device=dev).view(store)
+        if w.kv_dtype == "int8":  # codes, then 16 float32 scales per (block, head); every word NaN
+            words = (w.num_blocks, w.num_kv_heads, (w.block_size * w.head_dim + 64) // 4)
+            self.pk = torch.full(words, POISON_BITS["int8"], dtype=torch.int32, device=dev).view(torch.int8)
+        else:
+            shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+            ints = {"f32": torch.int32, "bf16": torch.int16, "e5m2": torch.uint8}[w.kv_dtype]
+            store = {"f32": torch.float32, "bf16": torch.bfloat16, "e5m2": torch.uint8}[w.kv_dtype]
+            self.pk = torch.full(shape, POISON_BITS[w.kv_dtype], dtype=ints, device=dev).view(store)
+        # an INT8 pool is written by the cache write's quantiser (no fused append)
+        self.fused = w.kv_dtype != "int8"
         self.pv = self.pk.clone()
         hist = write_plan(w, "cached")
         slots = pa.slot_mapping(torch.from_numpy(hist.cu).to(dev), torch.from_numpy(hist.end_pos).to(dev),
@@ -116,7 +129,7 @@ class Batch:
         self.args_append = (P(self.out), P(self.q), P(self.knew), P(self.vnew), P(self.pk), P(self.pv), P(self.tables),
                             mb, P(self.lens), n, hkv, g, d, bs, nb, ml, w.scale, qd, kd, partition,
                             pa.binding.PA_APPEND_SKIP_REDUCE, P(self.ws), self.ws.numel())
-        self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * d * 2 * KV_BYTES[w.kv_dtype]
+        self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * 2 * row_bytes(w)
 
 
 class VarlenBatch:
@@ -381,7 +394,7 @@ def main():
         bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check)
         return
     partition = args.partition if args.partition is not None else (w0.partition_size or -1)
-    pool_bytes = w0.num_blocks * w0.num_kv_heads * 16 * w0.head_dim * 2 * KV_BYTES[w0.kv_dtype]
+    pool_bytes = w0.num_blocks * w0.num_kv_heads * 16 * 2 * row_bytes(w0)
     reps = args.replicas or max(2, min(8, -(-1_200_000_000 // pool_bytes)))
     t_setup = time.perf_counter()
     batches = [Batch(w0 if r == 0 else make_config(args.config, replica=r), partition, pa, torch, to_dev)
@@ -400,10 +413,14 @@ def main():
         if b.split:
             check(lib.paged_attention_decode_reduce(*b.args_reduce, sh), "decode reduce")
 
-    def step_unfused(b):
+    def step_unfused(b, ev=None):
         check(lib.paged_kv_slot_mapping(*b.args_slot, sh), "slot mapping")
         check(lib.kv_cache_write(*b.args_write, sh), "cache write")
+        if ev is not None:
+            ev[0].record(stream)
         check(lib.paged_attention_decode_partitions(*b.args_parts, sh), "decode partitions")
+        if ev is not None:
+            ev[1].record(stream)
         if b.split:
             check(lib.paged_attention_decode_reduce(*b.args_reduce, sh), "decode reduce")
 
@@ -431,9 +448,11 @@ def main():
     # unfused path first (it also warms the clocks), then the roofline loop (a HIP event
     # pair around the partition kernel of every step), then the reported steps, back to
     # back with no events between launches
+    fused = batches[0].fused
+    main_step = step if fused else step_unfused
     ms_unfused, _, _ = timed(step_unfused, False)
-    _, _, kern_ms = timed(step, True)
-    ms_step, wall, _ = timed(step, False)
+    _, _, kern_ms = timed(main_step, True)
+    ms_step, wall, _ = timed(main_step, False)
     kern_avg = float(np.mean(kern_ms))
     step_bytes = float(np.mean([batches[i % reps].kv_bytes for i in range(args.steps)]))
     seqs = w0.num_seqs
@@ -469,7 +488,8 @@ def main():
             "context_lens": f"{int(w0.context_lens.min())}..{int(w0.context_lens.max())}",
             "partition_tokens": batches[0].resolved,
             "resident_batches": reps,
-            "step": "one launch: slot mapping + cache write of the newest token + decode attention" +
+            "step": ("one launch: slot mapping + cache write of the newest token + decode attention" if fused else
+                     "slot mapping + INT8 cache write (quantise) of the newest token + decode attention") +
                     (" (split-KV partitions) + the separate reduce kernel" if batches[0].split else ""),
         },
         "seq_steps_per_s": round(seqs / (ms_step * 1e-3), 1),
@@ -481,7 +501,7 @@ def main():
                              (" + separate reduce kernel" if batches[0].split else "")},
         "wall_s": round(wall, 4),
         "roofline": {
-            "kernel": "decode_partition_kernel (append mode)",
+            "kernel": "decode_partition_kernel" + (" (append mode)" if fused else " (INT8 pool)"),
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -540,24 +560,37 @@ def cpu_baseline(w, budget_s):
         while t_used < budget_s:
             sel = [(s0 + i) % w.num_seqs for i in range(8)]
             # history of these sequences (not timed: it is the state the step starts from)
-            pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
-                                 POISON_BITS[w.kv_dtype])
+            int8 = w.kv_dtype == "int8"
+            if int8:  # the oracle's INT8 pool: dequantised rows (code * scale), float64
+                pk = np.full((w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim), np.nan)
+            else:
+                pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                     POISON_BITS[w.kv_dtype])
             pv = pk.copy()
+
+            def write(pool, rows, slots):
+                if int8:
+                    codes, scales = oracle.quantize_int8(oracle.decode_storage(rows, w.src_dtype).astype(np.float32))
+                    keep = slots >= 0
+                    pool[slots[keep] // w.block_size, slots[keep] % w.block_size] = \
+                        oracle.dequantize_int8(codes[keep], scales[keep])
+                else:
+                    oracle.cache_write(pool, rows, slots, w.src_dtype, w.kv_dtype, w.block_size)
+
             hist = write_plan(w, "cached", sel)
             hs = oracle.slot_mapping(w.block_tables, hist.counts, hist.end_pos, w.block_size)
-            oracle.cache_write(pk, hist.k, hs, w.src_dtype, w.kv_dtype, w.block_size)
-            oracle.cache_write(pv, hist.v, hs, w.src_dtype, w.kv_dtype, w.block_size)
+            write(pk, hist.k, hs)
+            write(pv, hist.v, hs)
             new = write_plan(w, "new", sel)
             t0 = time.perf_counter()
             ns = oracle.slot_mapping(w.block_tables, new.counts, new.end_pos, w.block_size)
-            oracle.cache_write(pk, new.k, ns, w.src_dtype, w.kv_dtype, w.block_size)
-            oracle.cache_write(pv, new.v, ns, w.src_dtype, w.kv_dtype, w.block_size)
-            oracle.paged_decode(pk, pv, w.kv_dtype, q, w.q_dtype, w.block_tables, w.context_lens, w.block_size,
-                                w.scale, seqs=sel)
+            write(pk, new.k, ns)
+            write(pv, new.v, ns)
+            oracle.paged_decode(pk, pv, "f64" if int8 else w.kv_dtype, q, w.q_dtype, w.block_tables,
+                                w.context_lens, w.block_size, w.scale, seqs=sel)
             t_used += time.perf_counter() - t0
             done_seqs += len(sel)
-            done_bytes += int(w.context_lens[sel].astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 2 * \
-                KV_BYTES[w.kv_dtype]
+            done_bytes += int(w.context_lens[sel].astype(np.int64).sum()) * w.num_kv_heads * 2 * row_bytes(w)
             s0 += 8
     return {
         "value": round(done_bytes / t_used / 1e9, 4),

@@ -9,6 +9,8 @@
  *         sections 2.1.2 "Paged Attention", 2.2.1 "Flash Attention", 2.2.2 "GQA".
  *   [TACO] Taco-LLM article ("易用性对齐 vLLM，推理效率提升超200%，这款国产加速框架什么来头？"),
  *         section "使用 Prefix Cache 技术降低 TTFT".
+ *   [FW]  LLM inference frameworks overview (vLLM, LMDeploy, ...), section "LMDeploy": KV cache
+ *         INT8 quantisation; [OPT] 2.6 "低比特量化": low-bit formats cut memory and traffic.
  *
  * Data model
  *   Every sequence's keys and values live in fixed-size blocks of `block_size`
@@ -31,6 +33,21 @@
  *            cache write casts bf16 -> E5M2 by round-to-nearest-even without saturation
  *            (|x| >= 61440 -> inf, NaN -> sign|0x7F); reads widen exactly
  *            [CI KVCache Quant: cast on store, cast back on load].
+ *   PA_INT8  symmetric int8 codes with one float32 scale per (token, KV head) row
+ *            [FW LMDeploy: KV cache INT8; no page fixes the scheme, this is the library's].
+ *            The cache write computes, in float32 with round-to-nearest-even:
+ *                amax = max_d |x_d| (NaN elements ignored), inv = amax > 0 ? 127 / amax : 0,
+ *                code_d = clamp(rint(x_d * inv), -127, 127) (a NaN product gives -127),
+ *                scale = amax / 127;
+ *            a reader uses code * scale.  Pool layout (block_size must be 16):
+ *                cache[num_blocks][num_kv_heads][16 * head_dim + 64] bytes
+ *            each (block, KV head) tile holding the 16 x head_dim codes (token-major, as in
+ *            the other pools) and then 16 float32 scales, the scale of token t at float
+ *            index 4 * (t % 4) + t / 4 (so the scales of tokens r, r+4, r+8, r+12 are one
+ *            16-byte word).  Decode reads the codes as f16 and forms, per token, the
+ *            probability times the value scale in f16 (11 significant bits; p <= 256 with
+ *            the kernel's lazy running max): value rows need amax below 32000, and
+ *            products below 2^-14 keep only f16's subnormal precision.
  *
  * Conventions for every entry point
  *   - All pointers are device pointers unless stated; the caller owns every buffer.
@@ -48,7 +65,8 @@
  *     [0, min(max_context_len, max_blocks_per_seq * block_size)].  Results for such
  *     inputs are unspecified but no access leaves the buffers described here.
  *   - Supported now: block_size 16; head_dim 64 or 128; gqa_group 1, 2, 4, 8 or 16;
- *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2).
+ *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), and (BF16, INT8)
+ *     for the decode calls without append.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -62,7 +80,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum {
   PA_OK = 0,
@@ -73,7 +91,7 @@ typedef enum {
   PA_ERR_OUT_OF_BLOCKS = 5
 } pa_status_t;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E5M2 = 2 } pa_dtype_t;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E5M2 = 2, PA_INT8 = 3 } pa_dtype_t;
 
 /* Version of this header's ABI (PA_ABI_VERSION). */
 int pa_abi_version(void);
@@ -112,7 +130,8 @@ pa_status_t paged_kv_slot_mapping(int32_t* slot_mapping, const int32_t* cu_token
 
 /*
  * kv_cache_write -- scatter new key/value rows into the pools ("kernel 1").
- * [CI BlockedKeyValueCache; CI KVCache Quant: the writer casts to E5M2 on store]
+ * [CI BlockedKeyValueCache; CI KVCache Quant: the writer casts to E5M2 on store;
+ *  FW LMDeploy: INT8 KV cache]
  *
  *   key, value    [num_tokens][num_kv_heads][head_dim] of src_dtype, dense, 16-byte
  *                 aligned
@@ -120,8 +139,10 @@ pa_status_t paged_kv_slot_mapping(int32_t* slot_mapping, const int32_t* cu_token
  *   value_cache   [num_blocks][num_kv_heads][block_size][head_dim] of cache_dtype
  *   slot_mapping  int32 [num_tokens]; row r goes to block slot/block_size, offset
  *                 slot % block_size; slot < 0 or >= num_blocks*block_size skips the row
- *   (src, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2)}; a same-type write
- *   copies bits, the E5M2 cast is round-to-nearest-even (see above).
+ *   (src, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, INT8)}; a same-type
+ *   write copies bits, the E5M2 cast is round-to-nearest-even, an INT8 write quantises each
+ *   (token, KV head) row and stores its codes and scale (see above; block_size 16 and
+ *   head_dim 64 or 128 for INT8).
  *   Two rows with the same slot in one call race: the stored row is unspecified.
  */
 pa_status_t kv_cache_write(const void* key, const void* value, void* key_cache,
@@ -229,7 +250,8 @@ pa_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens
  * paged_attention_decode over all L tokens.  The result is bit-identical to
  * paged_kv_slot_mapping + kv_cache_write + paged_attention_decode with the same
  * partition size.  A sequence with L = 0 appends nothing.  A slot whose table entry is
- * outside [0, num_blocks) is not written.
+ * outside [0, num_blocks) is not written.  An INT8 pool is not supported here
+ * (PA_ERR_UNSUPPORTED): write its rows with kv_cache_write.
  *
  * flags: PA_APPEND_SKIP_REDUCE -- run only the streaming pass; the caller then runs
  *        paged_attention_decode_reduce (same arguments) when a sequence is split.
@@ -357,7 +379,8 @@ pa_status_t pa_bm_stats(const pa_block_manager* manager, int32_t* free_blocks, i
  * pairs[2i] -> block pairs[2i+1] (every KV head, every slot).  Carries out the copies that
  * pa_bm_append reports.  pairs: device int32 [2 * num_pairs]; a pair with an entry outside
  * [0, num_blocks) or src == dst is skipped; two pairs with the same destination race.
- * cache_dtype: PA_F32, PA_BF16 or PA_FP8_E5M2 (bytes are copied).
+ * cache_dtype: PA_F32, PA_BF16, PA_FP8_E5M2 or PA_INT8 (bytes are copied; an INT8 block
+ * carries its scales).
  */
 pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,

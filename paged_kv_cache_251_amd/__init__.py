@@ -9,14 +9,18 @@ from .binding import (  # noqa: F401
     PA_BF16,
     PA_F32,
     PA_FP8_E5M2,
+    PA_INT8,
     BlockManager,
     PagedAttnError,
     abi_version,
     alloc_workspace,
     auto_partition,
     copy_blocks,
+    int8_pool_split,
+    int8_scale_order,
     kv_cache_write,
     lib,
+    new_int8_pool,
     paged_attention_decode,
     paged_attention_decode_append,
     paged_attention_varlen,

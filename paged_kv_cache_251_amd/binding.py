@@ -16,7 +16,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
-PA_F32, PA_BF16, PA_FP8_E5M2 = 0, 1, 2
+PA_F32, PA_BF16, PA_FP8_E5M2, PA_INT8 = 0, 1, 2, 3
+INT8_BLOCK = 16  # tokens per block of an INT8 pool
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "device error",
           5: "out of blocks"}
 PA_ERR_OUT_OF_BLOCKS = 5
@@ -122,7 +123,42 @@ def dtype_code(t: torch.Tensor) -> int:
         return PA_BF16
     if t.dtype in (torch.uint8, torch.float8_e5m2):
         return PA_FP8_E5M2
+    if t.dtype == torch.int8:
+        return PA_INT8
     raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _pool_dims(cache: torch.Tensor):
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a pool: [nb, Hkv, B, D] of its element
+    type, or for INT8 int8 bytes [nb, Hkv, 16 * D + 64] (codes, then 16 float32 scales)."""
+    if cache.dtype == torch.int8:
+        _expect(cache.dim() == 3 and (cache.shape[2] - 64) % INT8_BLOCK == 0 and cache.shape[2] > 64,
+                "an INT8 pool is int8 [num_blocks, Hkv, 16 * D + 64]")
+        return cache.shape[0], cache.shape[1], INT8_BLOCK, (cache.shape[2] - 64) // INT8_BLOCK
+    _expect(cache.dim() == 4, "a pool is [num_blocks, Hkv, block_size, D]")
+    return tuple(cache.shape)
+
+
+def new_int8_pool(num_blocks: int, num_kv_heads: int, head_dim: int, device) -> torch.Tensor:
+    """Zeroed INT8 pool (codes and scales) for num_blocks blocks of 16 tokens."""
+    return torch.zeros((num_blocks, num_kv_heads, INT8_BLOCK * head_dim + 64), dtype=torch.int8, device=device)
+
+
+def int8_pool_split(pool: torch.Tensor):
+    """Views of an INT8 pool: codes [nb, Hkv, 16, D] (int8) and the scales [nb, Hkv, 16] (float32)
+    in their stored order -- the scale of token t at index 4 * (t % 4) + t // 4."""
+    nb, hkv, bs, d = _pool_dims(pool)
+    codes = pool[:, :, : bs * d].view(nb, hkv, bs, d)
+    scales = pool[:, :, bs * d:].view(torch.float32)
+    return codes, scales
+
+
+def int8_scale_order() -> list:
+    """Token of every stored scale slot: slot 4 * (t % 4) + t // 4 holds token t."""
+    order = [0] * INT8_BLOCK
+    for t in range(INT8_BLOCK):
+        order[4 * (t % 4) + t // 4] = t
+    return order
 
 
 def abi_version() -> int:
@@ -154,10 +190,10 @@ def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
     _dev(key, value, key_cache, value_cache, slot_mapping)
     _int32(slot_mapping)
     t, hkv, d = key.shape
-    nb, _, bs, _ = key_cache.shape
+    nb, phkv, bs, pd = _pool_dims(key_cache)
     _expect(value.shape == key.shape and value.dtype == key.dtype, "key and value rows differ")
     _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
-    _expect(key_cache.shape[1] == hkv and key_cache.shape[3] == d, "rows and pools disagree on Hkv / D")
+    _expect(phkv == hkv and pd == d, "rows and pools disagree on Hkv / D")
     _expect(slot_mapping.shape == (t,), "slot_mapping must be [num_tokens]")
     _check("kv_cache_write", lib().kv_cache_write(
         _ptr(key), _ptr(value), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), t, hkv, d, bs, nb,
@@ -188,9 +224,9 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
     _dev(query, key_cache, value_cache, block_tables, context_lens)
     _int32(block_tables, context_lens)
     n, hq, d = query.shape
-    nb, hkv, bs, _ = key_cache.shape
+    nb, hkv, bs, pd = _pool_dims(key_cache)
     _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
-    _expect(key_cache.shape[3] == d and hq % hkv == 0, "query and pools disagree on D / heads")
+    _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
     _expect(block_tables.dim() == 2 and block_tables.shape[0] == n and context_lens.shape == (n,),
             "block_tables [N, max_blocks], context_lens [N]")
     g = hq // hkv
@@ -220,9 +256,9 @@ def paged_attention_decode_append(query: torch.Tensor, key: torch.Tensor, value:
     _dev(query, key, value, key_cache, value_cache, block_tables, context_lens)
     _int32(block_tables, context_lens)
     n, hq, d = query.shape
-    nb, hkv, bs, _ = key_cache.shape
+    nb, hkv, bs, pd = _pool_dims(key_cache)
     _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
-    _expect(key_cache.shape[3] == d and hq % hkv == 0, "query and pools disagree on D / heads")
+    _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
     _expect(key.shape == (n, hkv, d) and value.shape == key.shape, "key/value rows must be [N, Hkv, D]")
     _expect(key.dtype == query.dtype and value.dtype == query.dtype, "key/value rows take the query dtype")
     _expect(block_tables.dim() == 2 and block_tables.shape[0] == n and context_lens.shape == (n,),
@@ -252,10 +288,10 @@ def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_c
     _dev(query, key_cache, value_cache, cu_seqlens_q, context_lens, block_tables)
     _int32(cu_seqlens_q, context_lens, block_tables)
     total_q, hq, d = query.shape
-    nb, hkv, bs, _ = key_cache.shape
+    nb, hkv, bs, pd = _pool_dims(key_cache)
     n = context_lens.shape[0]
     _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
-    _expect(key_cache.shape[3] == d and hq % hkv == 0, "query and pools disagree on D / heads")
+    _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
     _expect(cu_seqlens_q.shape == (n + 1,) and block_tables.dim() == 2 and block_tables.shape[0] == n,
             "cu_seqlens_q [N+1], context_lens [N], block_tables [N, max_blocks]")
     g = hq // hkv
@@ -349,8 +385,8 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, pairs: torch
     """Carry out block copies [(src, dst)] (int32 [n, 2] on the GPU) in both pools."""
     _dev(key_cache, value_cache, pairs)
     _int32(pairs)
-    _expect(key_cache.shape == value_cache.shape and key_cache.dim() == 4, "pools must be [blocks, heads, B, D]")
-    nb, hkv, bs, d = key_cache.shape
+    _expect(key_cache.shape == value_cache.shape and key_cache.dtype == value_cache.dtype, "pools differ")
+    nb, hkv, bs, d = _pool_dims(key_cache)
     _check("paged_kv_copy_blocks", lib().paged_kv_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(),
                                                                pairs.data_ptr(), pairs.numel() // 2, hkv, d, bs, nb,
                                                                dtype_code(key_cache), _stream()))

@@ -3,6 +3,8 @@
 // Colossal-Inference release post, "分块式KV缓存 (BlockedKeyValueCache)": logical blocks map
 // through a block table to physical blocks anywhere in the pool; "KV缓存量化 (KVCache
 // Quant)": the kernel that stores new keys and values casts them to FP8 E5M2 on the way.
+// LLM inference frameworks overview, "LMDeploy": an INT8 KV cache; the scheme (symmetric codes,
+// one float32 scale per (token, KV head) row) is this library's.
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -90,6 +92,60 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint4* __restric
   }
 }
 
+// bf16 rows -> INT8 pool.  D/8 consecutive lanes take one (token, KV head) row, 8 elements each
+// (one 16-byte load); the row's amax is reduced across them, then every lane stores its 8 codes
+// and the row's first lane the scale.  The maximum is taken on the bf16 magnitude patterns as
+// integers (order-preserving for non-NaN values; NaN mapped below every number), so NaN
+// elements are ignored whatever their payload and an all-NaN row gets a NaN amax.
+template <int D>
+__global__ __launch_bounds__(256) void cache_write_i8_kernel(const uint4* __restrict__ key,
+                                                             const uint4* __restrict__ value,
+                                                             uint8_t* __restrict__ key_cache,
+                                                             uint8_t* __restrict__ value_cache,
+                                                             const int32_t* __restrict__ slots, int32_t num_tokens,
+                                                             int32_t num_kv_heads, int32_t num_blocks) {
+  constexpr int LPR = D / 8;  // lanes per row; divides 64, so a row never straddles waves
+  constexpr int TILE = TileStride<KV_I8, D>::value;
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t total = (size_t)num_tokens * num_kv_heads * LPR;
+  if (i >= total) return;  // total is a multiple of LPR: a row's lanes leave together
+  const size_t row = i / LPR;
+  const int c = (int)(i % LPR);
+  const int t = (int)(row / num_kv_heads), h = (int)(row % num_kv_heads);
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * 16) return;  // same slot on every lane of the row
+  const int r = slot & 15;
+  const size_t tile = ((size_t)(slot >> 4) * num_kv_heads + h) * TILE;
+
+  auto quantize = [&](uint4 w, uint8_t* pool) {
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+    float x[8];
+    int key_max = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = bf16lo(words[k]);
+      x[2 * k + 1] = bf16hi(words[k]);
+      const int a0 = (int)(words[k] & 0x7FFFu), a1 = (int)((words[k] >> 16) & 0x7FFFu);
+      key_max = max(key_max, max(a0 > 0x7F80 ? -1 : a0, a1 > 0x7F80 ? -1 : a1));
+    }
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) key_max = max(key_max, __shfl_xor(key_max, off));
+    const float amax = key_max < 0 ? __builtin_nanf("") : as_f32((uint32_t)key_max << 16);
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float q = rintf(x[k] * inv);
+      const int code = q != q ? -127 : (int)fminf(fmaxf(q, -127.f), 127.f);
+      packed[k >> 2] |= ((uint32_t)code & 0xFFu) << (8 * (k & 3));
+    }
+    *reinterpret_cast<uint2*>(pool + tile + (size_t)r * D + (size_t)c * 8) = make_uint2(packed[0], packed[1]);
+    if (c == 0) *reinterpret_cast<float*>(pool + tile + 16 * D + 4 * (4 * (r & 3) + (r >> 2))) = amax / 127.0f;
+  };
+  quantize(key[i], key_cache);
+  quantize(value[i], value_cache);
+}
+
 hipError_t launch_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
                               const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks, int src_kind,
@@ -111,6 +167,12 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
   else if (src_kind == KV_BF16 && cache_kind == KV_E5M2)
     hipLaunchKernelGGL((cache_write_kernel<KV_BF16, KV_E5M2>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
                        slots, num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
+  else if (src_kind == KV_BF16 && cache_kind == KV_I8 && block_size == 16 && head_dim == 128)
+    hipLaunchKernelGGL((cache_write_i8_kernel<128>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc, slots,
+                       num_tokens, num_kv_heads, num_blocks);
+  else if (src_kind == KV_BF16 && cache_kind == KV_I8 && block_size == 16 && head_dim == 64)
+    hipLaunchKernelGGL((cache_write_i8_kernel<64>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc, slots,
+                       num_tokens, num_kv_heads, num_blocks);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -20,8 +20,10 @@
 //    by more than TAU (2^8): exact, since the same stale max is used for the numerator
 //    and the denominator, and it makes the rescale branch rare.
 //  * Probabilities reach the PV lanes by DPP row broadcast; V is accumulated in fp32
-//    (f32 / bf16 caches) or with f16 dot2 over token pairs (E5M2 cache, whose codes
-//    widen exactly to f16).
+//    (f32 / bf16 caches) or with f16 dot2 over token pairs (E5M2 and INT8 caches, whose
+//    codes widen exactly to f16).  An INT8 tile ends in its 16 row scales, ordered so that
+//    one 16-byte load gives a lane the scales of its row's four tokens: the key scale
+//    multiplies the finished dot product, the value scale the probability (in f16).
 //  * Rows, then waves, are merged at the end; a single partition writes the output,
 //    several write (o/l, m, l) to the workspace for the reduce kernel.
 #include <atomic>
@@ -70,12 +72,15 @@ struct DecodeTile {
   static constexpr int NDW = EPL * SZ / 4;    // dwords per lane per token row
   static constexpr int NL = 4;                // loads per 16-token tile (4 rows each)
   static constexpr int QDW = KV == KV_F32 ? EPL : EPL / 2;  // q dwords per head per lane
+  static constexpr bool F16_Q = KV == KV_E5M2 || KV == KV_I8;  // bf16 query widened to f16
+  static constexpr int SCW = KV == KV_I8 ? 4 : 1;              // scale dwords per lane per tile
+  static constexpr int TILE = TileStride<KV, D>::value;        // bytes per (block, KV head)
 };
 
 template <int KV, int D, int G, int W>
 __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodeParams p) {
   using T = DecodeTile<KV, D, G>;
-  constexpr int EPL = T::EPL, NDW = T::NDW, NL = T::NL, QDW = T::QDW, SZ = T::SZ;
+  constexpr int EPL = T::EPL, NDW = T::NDW, NL = T::NL, QDW = T::QDW, SZ = T::SZ, SCW = T::SCW;
   constexpr int S = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
 
   const int lane = threadIdx.x & 63;
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   // ---- the query group, in this lane's head order -------------------------------------
   // (raw loads only here; they are waited for after the first tile's loads are issued)
   uint32_t qv[G][QDW];
-  uint32_t qraw[G][KV == KV_E5M2 ? QDW : 1];
+  uint32_t qraw[G][T::F16_Q ? QDW : 1];
 #pragma unroll
   for (int k = 0; k < G; ++k) {
     const int h = head_of_slot<G>(col, k);
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   // b_new then comes from the new row instead of the cache (no read-after-write inside
   // the launch).  Lane (row, col) keeps columns col*EPL .. col*EPL+EPL-1 in cache format.
   const int pos_new = L - 1;
-  const bool appending = p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
+  const bool appending = KV != KV_I8 && p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
   const int b_new = appending ? pos_new / 16 : -1;
   const int r_new = pos_new & 15;
   uint32_t knew[NDW], vnew[NDW];
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
     } else if constexpr (KV == KV_BF16) {
       load_dw<NDW>(knew, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
       load_dw<NDW>(vnew, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
-    } else {
+    } else if constexpr (KV == KV_E5M2) {  // (an INT8 pool never appends)
       load_dw<2 * NDW>(kraw, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
       load_dw<2 * NDW>(vraw, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
     }
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   // and make every query register ready before the tile loop (so that the loop's own
   // waits only count tile loads).
   auto finish_query = [&]() {
-    if constexpr (KV == KV_E5M2) {
+    if constexpr (T::F16_Q) {
 #pragma unroll
       for (int k = 0; k < G; ++k)
 #pragma unroll
@@ -203,25 +208,32 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   const int b_first = t0 / 16 + wave;
   const int b_end = (t1 + 15) / 16;
   const int* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const size_t tile_elems = (size_t)16 * D;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.key_cache);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
   const size_t lane_off = ((size_t)row * D + (size_t)col * EPL) * SZ;
 
-  auto load_tile = [&](int b, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW]) -> int {
+  // INT8 scales of this lane's row: tokens row, row+4, row+8, row+12 of the tile
+  const size_t scale_off = (size_t)16 * D + (size_t)row * 16;
+
+  auto load_tile = [&](int b, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW], uint32_t (&ks)[SCW],
+                       uint32_t (&vs)[SCW]) -> int {
     int phys = load_invariant(table + b);
     const bool ok = phys >= 0 && phys < p.num_blocks;
     phys = ok ? phys : 0;
-    const size_t off = (((size_t)phys * p.num_kv_heads + g) * tile_elems) * SZ + lane_off;
+    const size_t tile = ((size_t)phys * p.num_kv_heads + g) * T::TILE;
+    const size_t off = tile + lane_off;
 #pragma unroll
     for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(kd[i], kbase + off + (size_t)i * 4 * D * SZ);
+    if constexpr (KV == KV_I8) load_dw<4, PA_NT_LOADS>(ks, kbase + tile + scale_off);
 #pragma unroll
     for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(vd[i], vbase + off + (size_t)i * 4 * D * SZ);
+    if constexpr (KV == KV_I8) load_dw<4, PA_NT_LOADS>(vs, vbase + tile + scale_off);
     __builtin_amdgcn_sched_barrier(0);  // issue the tile before any math that follows
     return ok;
   };
 
-  auto compute_tile = [&](int b, bool ok, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW]) {
+  auto compute_tile = [&](int b, bool ok, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW], uint32_t (&ks)[SCW],
+                          uint32_t (&vs)[SCW]) {
     // valid tokens of this tile: [b*16, min(b*16+16, t1)), all of them if the block is valid
     const int tok_lim = ok ? min(16, t1 - b * 16) : 0;
     if (b == b_new) {  // the appended token: use its row, not the (not yet written) slot
@@ -239,10 +251,21 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float r[G];
+      uint32_t kh[KV == KV_I8 ? 2 * NDW : 1];  // INT8 codes of this token as f16 pairs
+      if constexpr (KV == KV_I8) {
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) {
+          kh[2 * j] = i8_pair_lo(kd[i][j]);
+          kh[2 * j + 1] = i8_pair_hi(kd[i][j]);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         float a = 0.f;
-        if constexpr (KV == KV_F32) {
+        if constexpr (KV == KV_I8) {
+#pragma unroll
+          for (int j = 0; j < 2 * NDW; ++j) a = dot2_f16(qv[k][j], kh[j], a);
+        } else if constexpr (KV == KV_F32) {
 #pragma unroll
           for (int j = 0; j < EPL; ++j) a = fmaf(as_f32(qv[k][j]), as_f32(kd[i][j]), a);
         } else if constexpr (KV == KV_BF16) {
@@ -259,7 +282,8 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       }
       row_reduce_heads<G>(r);
       const bool live = (4 * i + row) < tok_lim;
-      sc[i] = live ? r[0] * p.scale_log2 : -__builtin_inff();
+      const float sl = KV == KV_I8 ? as_f32(ks[KV == KV_I8 ? i : 0]) * p.scale_log2 : p.scale_log2;
+      sc[i] = live ? r[0] * sl : -__builtin_inff();
     }
     // online softmax for this row's own head, threshold rescale
     float bmax = sc[0];
@@ -281,7 +305,9 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
     float pr[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) pr[i] = (4 * i + row) < tok_lim ? fast_exp2(sc[i] - m_own) : 0.f;
-    if (tok_lim < 16) {  // tail or skipped block: unwritten slots may hold anything (NaN)
+    // tail or skipped block: unwritten slots may hold anything (NaN); INT8 codes are always
+    // finite, and there the scale is masked instead (below)
+    if (KV != KV_I8 && tok_lim < 16) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const bool live = (4 * i + row) < tok_lim;
@@ -289,7 +315,29 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
         for (int j = 0; j < NDW; ++j) vd[i][j] = live ? vd[i][j] : 0u;
       }
     }
-    if constexpr (KV == KV_E5M2) {
+    if constexpr (KV == KV_I8) {
+#pragma unroll
+      for (int i = 0; i < NL; i += 2) {
+        const float w0 = (4 * i + row) < tok_lim ? pr[i] * as_f32(vs[i]) : 0.f;
+        const float w1 = (4 * i + 4 + row) < tok_lim ? pr[i + 1] * as_f32(vs[i + 1]) : 0.f;
+        l_own += pr[i] + pr[i + 1];
+        const uint32_t pp = pack_f16x2_rne(w0, w1);
+        uint32_t vp[EPL];
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) {
+          vp[4 * j + 0] = i8_cross_pair<0>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 1] = i8_cross_pair<1>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 2] = i8_cross_pair<2>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 3] = i8_cross_pair<3>(vd[i][j], vd[i + 1][j]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const uint32_t ph = bcast_head_u32<G>(pp, h);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = dot2_f16(ph, vp[e], acc[h][e]);
+        }
+      }
+    } else if constexpr (KV == KV_E5M2) {
 #pragma unroll
       for (int i = 0; i < NL; i += 2) {
         const uint32_t pp = pack_f16x2_rne(pr[i], pr[i + 1]);
@@ -342,24 +390,25 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
     const int ntiles = b_first < b_end ? (b_end - b_first + W - 1) / W : 0;
     if (ntiles > 0) {
       uint32_t ka[NL][NDW], va[NL][NDW], kb[NL][NDW], vb[NL][NDW];
+      uint32_t ksa[SCW], vsa[SCW], ksb[SCW], vsb[SCW];
       int b = b_first;
-      int oka = load_tile(b, ka, va), okb;
+      int oka = load_tile(b, ka, va, ksa, vsa), okb;
       finish_query();
       finish_append();
       int i = 0;
       for (; i + 2 < ntiles; i += 2) {
-        okb = load_tile(b + W, kb, vb);
-        compute_tile(b, oka, ka, va);
-        oka = load_tile(b + 2 * W, ka, va);
-        compute_tile(b + W, okb, kb, vb);
+        okb = load_tile(b + W, kb, vb, ksb, vsb);
+        compute_tile(b, oka, ka, va, ksa, vsa);
+        oka = load_tile(b + 2 * W, ka, va, ksa, vsa);
+        compute_tile(b + W, okb, kb, vb, ksb, vsb);
         b += 2 * W;
       }
       if (i + 1 < ntiles) {
-        okb = load_tile(b + W, kb, vb);
-        compute_tile(b, oka, ka, va);
-        compute_tile(b + W, okb, kb, vb);
+        okb = load_tile(b + W, kb, vb, ksb, vsb);
+        compute_tile(b, oka, ka, va, ksa, vsa);
+        compute_tile(b + W, okb, kb, vb, ksb, vsb);
       } else {
-        compute_tile(b, oka, ka, va);
+        compute_tile(b, oka, ka, va, ksa, vsa);
       }
     }
   }
@@ -594,10 +643,12 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head
     if (kv_kind == KV_F32) return launch_parts_kv_d<KV_F32, 128>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_BF16) return launch_parts_kv_d<KV_BF16, 128>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_E5M2) return launch_parts_kv_d<KV_E5M2, 128>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_I8) return launch_parts_kv_d<KV_I8, 128>(p, gqa, num_seqs, stream);
   } else if (head_dim == 64) {
     if (kv_kind == KV_F32) return launch_parts_kv_d<KV_F32, 64>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_BF16) return launch_parts_kv_d<KV_BF16, 64>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_E5M2) return launch_parts_kv_d<KV_E5M2, 64>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_I8) return launch_parts_kv_d<KV_I8, 64>(p, gqa, num_seqs, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -16,6 +16,15 @@ template <>
 struct KvBytes<KV_BF16> { static constexpr int value = 2; };
 template <>
 struct KvBytes<KV_E5M2> { static constexpr int value = 1; };
+template <>
+struct KvBytes<KV_I8> { static constexpr int value = 1; };
+
+// Bytes from the start of one (block, KV head) tile of 16 x D elements to the next: the tile,
+// and for int8 the 16 float32 scales that follow it.
+template <int KV, int D>
+struct TileStride {
+  static constexpr int value = 16 * D * KvBytes<KV>::value + (KV == KV_I8 ? 64 : 0);
+};
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
@@ -168,6 +177,22 @@ __device__ __forceinline__ uint32_t e5m2_cross_pair(uint32_t a, uint32_t b) {
   // v_perm: bytes 0-3 select from the second source (a), 4-7 from the first (b)
   constexpr uint32_t sel = 0x0Cu | ((uint32_t)J << 8) | (0x0Cu << 16) | ((uint32_t)(4 + J) << 24);
   return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// int8 codes -> f16x2 words, exact: with the sign bit of a byte flipped and 0x64 as the upper
+// byte, an f16 holds 1024 + 128 + code; subtracting 1152 (packed f16) leaves the code.
+__device__ __forceinline__ uint32_t i8_finish(uint32_t magic) {
+  const f16x2_t r = __builtin_bit_cast(f16x2_t, magic ^ 0x64806480u) - f16x2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, r);
+}
+// bytes 0, 1 (lo) or 2, 3 (hi) of w as an f16x2 word
+__device__ __forceinline__ uint32_t i8_pair_lo(uint32_t w) { return i8_finish(__builtin_amdgcn_perm(0u, w, 0x0C010C00u)); }
+__device__ __forceinline__ uint32_t i8_pair_hi(uint32_t w) { return i8_finish(__builtin_amdgcn_perm(0u, w, 0x0C030C02u)); }
+// (byte j of a, byte j of b) as an f16x2 word, low half from a
+template <int J>
+__device__ __forceinline__ uint32_t i8_cross_pair(uint32_t a, uint32_t b) {
+  constexpr uint32_t sel = (uint32_t)J | (0x0Cu << 8) | ((uint32_t)(4 + J) << 16) | (0x0Cu << 24);
+  return i8_finish(__builtin_amdgcn_perm(b, a, sel));
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

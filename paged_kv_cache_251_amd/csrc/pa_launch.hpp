@@ -7,7 +7,8 @@
 namespace pa {
 
 // Element type of a pool (values match pa_dtype_t).
-enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_E5M2 = 2 };
+// KV_I8: int8 codes with one float32 scale per (token, KV head) after each (block, head) tile
+enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_E5M2 = 2, KV_I8 = 3 };
 
 struct DecodeParams {
   void* out;

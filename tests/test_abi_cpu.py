@@ -46,7 +46,7 @@ def test_binding_signatures_cover_the_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
     assert lib.pa_status_string(5) == b"out of blocks"
     assert lib.pa_status_string(0) == b"ok"
     assert lib.pa_status_string(3) == b"workspace too small"
@@ -72,6 +72,7 @@ def _decode(lib, **kw):
     (dict(kc=FAKE + 8), 1), (dict(part=16, maxl=64), 1),  # split needs a workspace
     (dict(part=16, maxl=64, ws=FAKE, wsb=16), 3), (dict(part=16, maxl=64, ws=FAKE + 64, wsb=1 << 20), 1),
     (dict(nb=1 << 28), 2), (dict(n=70000), 2),
+    (dict(qd=0, kd=3), 2), (dict(qd=3, kd=3), 2), (dict(qd=2, kd=3), 2),  # INT8 pools take bf16 queries
 ])
 def test_decode_rejects_bad_arguments_on_host(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -95,6 +96,23 @@ def test_cache_write_rejects_bad_arguments_on_host(lib):
     assert f(None, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 1, 1, None) == 1
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 16, 8, 1, 1, None) == 2  # 8-byte rows
     assert f(None, None, None, None, None, 0, 2, 128, 16, 8, 1, 1, None) == 0  # nothing to write
+    # INT8 pools: bf16 rows only, 16-token blocks, head_dim 64 or 128
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 0, 3, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 32, 8, 1, 3, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 96, 16, 8, 1, 3, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 1, 4, None) == 1  # unknown dtype
+
+
+def test_int8_pool_is_rejected_where_unsupported(lib):
+    # the fused append writes rows in the query dtype's cast; an INT8 pool is written by kv_cache_write
+    app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
+                                            64, 0.1, 1, 3, 0, 0, None, 0, None)
+    assert app == 2 and b"INT8" in lib.pa_last_error()
+    var = lib.paged_attention_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 2, 2, 2, 128, 16, 8, 64,
+                                     0.1, 1, 1, 3, 0, None, 0, None)
+    assert var == 2
+    cp = lib.paged_kv_copy_blocks(FAKE, FAKE, FAKE, 1, 2, 128, 32, 8, 3, None)
+    assert cp == 2
 
 
 def test_slot_mapping_rejects_bad_arguments_on_host(lib):
