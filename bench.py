@@ -495,10 +495,11 @@ def main():
         "seq_steps_per_s": round(seqs / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(step_bytes),
-        "unfused": {"ms_per_step": round(ms_unfused, 5),
-                    "GB_per_s": round(step_bytes / (ms_unfused * 1e-3) / 1e9, 2),
-                    "calls": "paged_kv_slot_mapping + kv_cache_write + decode partitions" +
-                             (" + separate reduce kernel" if batches[0].split else "")},
+        "unfused": None if not fused else {
+            "ms_per_step": round(ms_unfused, 5),
+            "GB_per_s": round(step_bytes / (ms_unfused * 1e-3) / 1e9, 2),
+            "calls": "paged_kv_slot_mapping + kv_cache_write + decode partitions" +
+                     (" + separate reduce kernel" if batches[0].split else "")},
         "wall_s": round(wall, 4),
         "roofline": {
             "kernel": "decode_partition_kernel" + (" (append mode)" if fused else " (INT8 pool)"),

@@ -77,8 +77,15 @@ struct DecodeTile {
   static constexpr int TILE = TileStride<KV, D>::value;        // bytes per (block, KV head)
 };
 
+// The INT8 kernels with up to 4 heads per group are held to 128 VGPRs (4 waves per SIMD
+// instead of 3; the few values spilled are outside the loop); larger groups need the registers.
+#ifndef PA_I8_WAVES_PER_EU
+#define PA_I8_WAVES_PER_EU 4
+#endif
+
 template <int KV, int D, int G, int W>
-__global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_EU : 1) void decode_partition_kernel(
+    const DecodeParams p) {
   using T = DecodeTile<KV, D, G>;
   constexpr int EPL = T::EPL, NDW = T::NDW, NL = T::NL, QDW = T::QDW, SZ = T::SZ, SCW = T::SCW;
   constexpr int S = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
@@ -184,12 +191,27 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
   // After the first tile is in flight: widen a bf16 query to f16 pairs for an E5M2 cache,
   // and make every query register ready before the tile loop (so that the loop's own
   // waits only count tile loads).
+  // INT8: the keys enter the dot products as 1152 + code (see i8_biased_lo); q_bias is
+  // -1152 * sum_d q[h][d] for the head h whose score this lane holds after the row reduction.
+  float q_bias = 0.f;
   auto finish_query = [&]() {
     if constexpr (T::F16_Q) {
 #pragma unroll
       for (int k = 0; k < G; ++k)
 #pragma unroll
         for (int j = 0; j < QDW; ++j) qv[k][j] = pack_f16x2_rne(bf16lo(qraw[k][j]), bf16hi(qraw[k][j]));
+    }
+    if constexpr (KV == KV_I8) {
+      float qs[G];
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < QDW; ++j) a += f16lo(qv[k][j]) + f16hi(qv[k][j]);
+        qs[k] = a;
+      }
+      row_reduce_heads<G>(qs);
+      q_bias = -1152.0f * qs[0];
     }
 #pragma unroll
     for (int k = 0; k < G; ++k)
@@ -199,6 +221,9 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
 
   float m_own = -__builtin_inff();  // running max (log2 domain) of this row's own head
   float l_own = 0.f;                // running sum of 2^(S - m_own) over this row's tokens
+  // INT8 values enter the PV products as 1152 + code: w_own is the running sum of this row's
+  // f16 weights p * scale (own head), and 1152 * w_own is taken off the accumulators at the end
+  float w_own = 0.f;
   float acc[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -251,12 +276,13 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float r[G];
-      uint32_t kh[KV == KV_I8 ? 2 * NDW : 1];  // INT8 codes of this token as f16 pairs
+      uint32_t kh[KV == KV_I8 ? 2 * NDW : 1];  // INT8 codes of this token as biased f16 pairs
       if constexpr (KV == KV_I8) {
 #pragma unroll
         for (int j = 0; j < NDW; ++j) {
-          kh[2 * j] = i8_pair_lo(kd[i][j]);
-          kh[2 * j + 1] = i8_pair_hi(kd[i][j]);
+          const uint32_t wx = kd[i][j] ^ 0x80808080u;
+          kh[2 * j] = i8_biased_lo(wx);
+          kh[2 * j + 1] = i8_biased_hi(wx);
         }
       }
 #pragma unroll
@@ -282,8 +308,11 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       }
       row_reduce_heads<G>(r);
       const bool live = (4 * i + row) < tok_lim;
-      const float sl = KV == KV_I8 ? as_f32(ks[KV == KV_I8 ? i : 0]) * p.scale_log2 : p.scale_log2;
-      sc[i] = live ? r[0] * sl : -__builtin_inff();
+      if constexpr (KV == KV_I8) {
+        sc[i] = live ? (r[0] + q_bias) * (as_f32(ks[i]) * p.scale_log2) : -__builtin_inff();
+      } else {
+        sc[i] = live ? r[0] * p.scale_log2 : -__builtin_inff();
+      }
     }
     // online softmax for this row's own head, threshold rescale
     float bmax = sc[0];
@@ -294,6 +323,7 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       const float mn = need ? bmax : m_own;
       const float alpha = need ? fast_exp2(m_own - mn) : 1.f;
       l_own *= alpha;
+      if constexpr (KV == KV_I8) w_own *= alpha;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float ah = bcast_head<G>(alpha, h);
@@ -322,13 +352,14 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
         const float w1 = (4 * i + 4 + row) < tok_lim ? pr[i + 1] * as_f32(vs[i + 1]) : 0.f;
         l_own += pr[i] + pr[i + 1];
         const uint32_t pp = pack_f16x2_rne(w0, w1);
+        w_own = dot2_f16(pp, 0x3C003C00u, w_own);  // + both f16 weights (times 1.0)
         uint32_t vp[EPL];
 #pragma unroll
         for (int j = 0; j < NDW; ++j) {
-          vp[4 * j + 0] = i8_cross_pair<0>(vd[i][j], vd[i + 1][j]);
-          vp[4 * j + 1] = i8_cross_pair<1>(vd[i][j], vd[i + 1][j]);
-          vp[4 * j + 2] = i8_cross_pair<2>(vd[i][j], vd[i + 1][j]);
-          vp[4 * j + 3] = i8_cross_pair<3>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 0] = i8_biased_cross_pair<0>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 1] = i8_biased_cross_pair<1>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 2] = i8_biased_cross_pair<2>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 3] = i8_biased_cross_pair<3>(vd[i][j], vd[i + 1][j]);
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -410,6 +441,15 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(const DecodePa
       } else {
         compute_tile(b, oka, ka, va, ksa, vsa);
       }
+    }
+  }
+
+  if constexpr (KV == KV_I8) {  // remove the bias the INT8 values carried into the accumulators
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float bh = -1152.0f * bcast_head<G>(w_own, h);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] += bh;
     }
   }
 

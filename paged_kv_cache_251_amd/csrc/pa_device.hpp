@@ -195,6 +195,19 @@ __device__ __forceinline__ uint32_t i8_cross_pair(uint32_t a, uint32_t b) {
   return i8_finish(__builtin_amdgcn_perm(b, a, sel));
 }
 
+// Biased form for dot products: with wx = w ^ 0x80808080 (each code's sign bit flipped), the
+// upper byte 0x64 comes from the constant operand, and each f16 holds 1152 + code exactly; a
+// dot product against q then carries 1152 * sum(q), which the caller subtracts once.
+__device__ __forceinline__ uint32_t i8_biased_lo(uint32_t wx) { return __builtin_amdgcn_perm(0x64646464u, wx, 0x04010400u); }
+__device__ __forceinline__ uint32_t i8_biased_hi(uint32_t wx) { return __builtin_amdgcn_perm(0x64646464u, wx, 0x04030402u); }
+
+// (byte j of a, byte j of b) as biased f16 values (1152 + code), low half from a
+template <int J>
+__device__ __forceinline__ uint32_t i8_biased_cross_pair(uint32_t a, uint32_t b) {
+  constexpr uint32_t sel = (uint32_t)J | (0x0Cu << 8) | ((uint32_t)(4 + J) << 16) | (0x0Cu << 24);
+  return __builtin_amdgcn_perm(b, a, sel) ^ 0x64806480u;
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
                                          false);
