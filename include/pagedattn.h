@@ -6,7 +6,8 @@
  *         sections "分块式KV缓存 (BlockedKeyValueCache)", "KV缓存量化 (KVCache Quant)",
  *         "分页注意力算法 (PagedAttention)", "连续批量化算法 (Continuous Batching)".
  *   [OPT] LLM inference optimisation overview ("AI 大模型推理优化技术详解"),
- *         sections 2.1.2 "Paged Attention", 2.2.1 "Flash Attention", 2.2.2 "GQA".
+ *         sections 2.1.2 "Paged Attention", 2.2.1 "Flash Attention", 2.2.2 "GQA",
+ *         2.4 "服务" (Continuous Batching, Dynamic Batching).
  *   [TACO] Taco-LLM article ("易用性对齐 vLLM，推理效率提升超200%，这款国产加速框架什么来头？"),
  *         section "使用 Prefix Cache 技术降低 TTFT".
  *   [FW]  LLM inference frameworks overview (vLLM, LMDeploy, ...), section "LMDeploy": KV cache
@@ -385,6 +386,112 @@ pa_status_t pa_bm_stats(const pa_block_manager* manager, int32_t* free_blocks, i
 pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                  pa_dtype_t cache_dtype, hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------------------
+ * Step scheduler (host side): which sequences run in each step, for continuous batching.
+ * [CI Continuous Batching: prefill and decode are computed apart, without padding, and a
+ *  prefill step runs when the inputs waiting for prefill reach a set ratio, so that most
+ *  steps are fast decode steps; OPT 2.4, Continuous Batching: step-level scheduling over a
+ *  Running and a Waiting queue, a finished sequence leaves Running and a waiting one takes its
+ *  place; OPT 2.4, Dynamic Batching: after every step the Running queue grows or shrinks with
+ *  the free memory; OPT 2.1.2: block-granular accounting tells how many more blocks fit (no
+ *  overflow), and max_num_batch_tokens bounds the tokens of one batch]
+ *
+ * A request is a prompt of token ids and a budget of new tokens.  Waiting is a FIFO of
+ * requests holding no blocks; Running holds the admitted sequences (in admission order), all
+ * of whose K/V except their newest token are in the cache.  Each pa_sched_step makes one step:
+ *   - Prefill step, when Waiting is not empty, Running has room (< max_running) and either
+ *     Running is empty or |Waiting| >= prefill_ratio * |Running|: requests are admitted from
+ *     the head of Waiting, in order, while Running has room, the step's known-token total
+ *     stays within max_batch_tokens (the first admitted request always fits, see add) and the
+ *     block manager can hold the sequence (pa_bm_add_sequence with its token ids, so a cached
+ *     prefix is reused).  The first request that does not fit ends admission.  Each admitted
+ *     sequence's query rows are its tokens past the reused prefix.  If nothing is admitted the
+ *     step is a decode step instead.
+ *   - Decode step: every running sequence, in admission order, appends its newest token
+ *     (pa_bm_append; a copy on write is reported in copies) and has it as its one query row.
+ *     When the pool cannot supply a block, the most recently admitted running sequence is
+ *     preempted (its blocks released, its known tokens -- prompt and generated -- put back at
+ *     the head of Waiting, to be prefilled again), until the append succeeds or the appending
+ *     sequence itself was preempted.
+ *   - Idle step (kind PA_STEP_IDLE): nothing to run.
+ * pa_sched_commit then takes, for every sequence of that step's batch in its order, the token
+ * it produced and whether it finished (for instance an end-of-sequence token).  A sequence
+ * also finishes when it has produced max_new_tokens tokens.  Finished sequences release their
+ * blocks (prefix-registered blocks stay cached) and leave Running.  A step must be committed
+ * before the next one (PA_ERR_INVALID_ARGUMENT otherwise); a step with no sequences needs no
+ * commit.
+ * The manager passed at creation is used only by the scheduler while it exists (sequence ids
+ * are the request ids).  Not thread-safe.
+ * ---------------------------------------------------------------------------------------
+ */
+typedef struct pa_scheduler pa_scheduler;
+
+typedef struct {
+  int32_t max_running;         /* most sequences in Running (> 0) */
+  int32_t max_batch_tokens;    /* most known tokens admitted by one prefill step (> 0) */
+  float prefill_ratio;         /* > 0, finite */
+  int32_t max_blocks_per_seq;  /* width of the block tables a step fills (> 0) */
+} pa_sched_config;
+
+#define PA_STEP_IDLE 0
+#define PA_STEP_PREFILL 1
+#define PA_STEP_DECODE 2
+
+/*
+ * One step's batch, in host arrays the caller owns.  Capacities (set by the caller, checked
+ * before anything changes): seq_ids, context_lens: max_running entries; cu_seqlens_q:
+ * max_running + 1; block_tables: max_running * max_blocks_per_seq (row-major, -1 past each
+ * sequence's blocks); input_tokens: max(max_batch_tokens, max_running); copies: 2 *
+ * max_running; preempted: max_running.  Outputs feed paged_kv_slot_mapping (cu_tokens =
+ * cu_seqlens_q, end_pos = context_lens), kv_cache_write and paged_attention_varlen (decode
+ * steps may also use paged_attention_decode), after paged_kv_copy_blocks of the copies.
+ */
+typedef struct {
+  int64_t* seq_ids;
+  int32_t* cu_seqlens_q;
+  int32_t* context_lens;
+  int32_t* block_tables;
+  int32_t* input_tokens;  /* token id of every query row, packed like the rows */
+  int32_t* copies;        /* (src, dst) block pairs */
+  int64_t* preempted;     /* requests moved back to Waiting during this step */
+  int32_t kind;           /* PA_STEP_* */
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t max_q_len;
+  int32_t max_context_len;
+  int32_t num_copies;
+  int32_t num_preempted;
+} pa_sched_batch;
+
+/* A scheduler over `manager` (which must outlive it) with the given limits. */
+pa_status_t pa_sched_create(const pa_sched_config* config, pa_block_manager* manager, pa_scheduler** scheduler);
+void pa_sched_destroy(pa_scheduler* scheduler);
+
+/*
+ * Queue a request at the tail of Waiting: request_id (not in use), prompt (host, prompt_len
+ * >= 1 token ids), max_new_tokens >= 1.  prompt_len + max_new_tokens - 1 (the most tokens a
+ * prefill of this request can carry, after a preemption) must be at most max_batch_tokens and
+ * fit max_blocks_per_seq blocks (PA_ERR_UNSUPPORTED otherwise).
+ */
+pa_status_t pa_sched_add_request(pa_scheduler* scheduler, int64_t request_id, const int32_t* prompt,
+                                 int32_t prompt_len, int32_t max_new_tokens);
+
+/* Make the next step (see above) and describe it in *batch. */
+pa_status_t pa_sched_step(pa_scheduler* scheduler, pa_sched_batch* batch);
+
+/*
+ * Results of the last step: next_tokens[i] and finished[i] (0 or 1; may be null: none
+ * finished early) for the i-th sequence of its batch, num_seqs entries.
+ */
+pa_status_t pa_sched_commit(pa_scheduler* scheduler, const int32_t* next_tokens, const uint8_t* finished,
+                            int32_t num_seqs);
+
+/* Requests waiting, sequences running, requests finished and preemptions so far.  Any pointer
+ * may be null. */
+pa_status_t pa_sched_stats(const pa_scheduler* scheduler, int32_t* waiting, int32_t* running, int64_t* finished,
+                           int64_t* preemptions);
 
 #ifdef __cplusplus
 }

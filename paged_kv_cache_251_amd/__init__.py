@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     PA_INT8,
     BlockManager,
     PagedAttnError,
+    Scheduler,
     abi_version,
     alloc_workspace,
     auto_partition,

@@ -25,6 +25,21 @@ PA_ERR_OUT_OF_BLOCKS = 5
 _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 _i64, _pi32 = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
 
+
+class SchedConfig(ctypes.Structure):
+    """pa_sched_config"""
+    _fields_ = [("max_running", ctypes.c_int32), ("max_batch_tokens", ctypes.c_int32),
+                ("prefill_ratio", ctypes.c_float), ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+class SchedBatch(ctypes.Structure):
+    """pa_sched_batch"""
+    _fields_ = [("seq_ids", ctypes.POINTER(ctypes.c_int64)), ("cu_seqlens_q", _pi32), ("context_lens", _pi32),
+                ("block_tables", _pi32), ("input_tokens", _pi32), ("copies", _pi32),
+                ("preempted", ctypes.POINTER(ctypes.c_int64)), ("kind", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("total_q", ctypes.c_int32), ("max_q_len", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("num_copies", ctypes.c_int32), ("num_preempted", ctypes.c_int32)]
+
 # name -> (restype, argtypes), in header order
 SIGNATURES = {
     "pa_abi_version": (ctypes.c_int, []),
@@ -57,7 +72,15 @@ SIGNATURES = {
     "pa_bm_block_table": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _pi32, _pi32]),
     "pa_bm_stats": (ctypes.c_int, [_vp, _pi32, _pi32, _pi32]),
     "paged_kv_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]),
+    "pa_sched_create": (ctypes.c_int, [ctypes.POINTER(SchedConfig), _vp, ctypes.POINTER(_vp)]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_add_request": (ctypes.c_int, [_vp, _i64, _pi32, _i32, _i32]),
+    "pa_sched_step": (ctypes.c_int, [_vp, ctypes.POINTER(SchedBatch)]),
+    "pa_sched_commit": (ctypes.c_int, [_vp, _pi32, ctypes.POINTER(ctypes.c_uint8), _i32]),
+    "pa_sched_stats": (ctypes.c_int, [_vp, _pi32, _pi32, ctypes.POINTER(ctypes.c_int64),
+                                      ctypes.POINTER(ctypes.c_int64)]),
 }
+PA_STEP_IDLE, PA_STEP_PREFILL, PA_STEP_DECODE = 0, 1, 2
 PA_APPEND_SKIP_REDUCE = 1
 
 
@@ -390,3 +413,74 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, pairs: torch
     _check("paged_kv_copy_blocks", lib().paged_kv_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(),
                                                                pairs.data_ptr(), pairs.numel() // 2, hkv, d, bs, nb,
                                                                dtype_code(key_cache), _stream()))
+
+
+# ------------------------------------------------------------------------------ step scheduler
+class Scheduler:
+    """Host step scheduler of the library (pa_sched_*) over a BlockManager: continuous batching
+    with Running / Waiting queues, the prefill-ratio trigger and block-budget admission."""
+
+    def __init__(self, manager: BlockManager, max_running: int, max_batch_tokens: int, prefill_ratio: float,
+                 max_blocks_per_seq: int):
+        import numpy as np
+
+        cfg = SchedConfig(max_running, max_batch_tokens, prefill_ratio, max_blocks_per_seq)
+        h = _vp()
+        _check("pa_sched_create", lib().pa_sched_create(ctypes.byref(cfg), manager._h, ctypes.byref(h)))
+        self._h = h
+        self.manager = manager  # keeps the manager alive as long as the scheduler
+        self.max_running, self.max_blocks = max_running, max_blocks_per_seq
+        ntok = max(max_batch_tokens, max_running)
+        self._arr = dict(
+            seq_ids=np.zeros(max_running, np.int64), cu=np.zeros(max_running + 1, np.int32),
+            lens=np.zeros(max_running, np.int32), tables=np.zeros(max_running * max_blocks_per_seq, np.int32),
+            tokens=np.zeros(ntok, np.int32), copies=np.zeros(2 * max_running, np.int32),
+            preempted=np.zeros(max_running, np.int64))
+        a = self._arr
+        p32 = lambda x: x.ctypes.data_as(_pi32)
+        p64 = lambda x: x.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        self._batch = SchedBatch(p64(a["seq_ids"]), p32(a["cu"]), p32(a["lens"]), p32(a["tables"]), p32(a["tokens"]),
+                                 p32(a["copies"]), p64(a["preempted"]))
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_sched_destroy(self._h)
+            self._h = _vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_request(self, request_id: int, prompt, max_new_tokens: int) -> None:
+        arr, n = _ids(prompt)
+        _check("pa_sched_add_request", lib().pa_sched_add_request(self._h, request_id, arr, n, max_new_tokens))
+
+    def step(self) -> dict:
+        """The next step: kind, seq_ids, cu_seqlens_q, context_lens, block_tables [N, max_blocks],
+        input_tokens, copies [(src, dst)], preempted, max_q_len, max_context_len (host copies)."""
+        b = self._batch
+        _check("pa_sched_step", lib().pa_sched_step(self._h, ctypes.byref(b)))
+        a, n = self._arr, b.num_seqs
+        return dict(kind=b.kind, seq_ids=a["seq_ids"][:n].copy(), cu_seqlens_q=a["cu"][: n + 1].copy(),
+                    context_lens=a["lens"][:n].copy(),
+                    block_tables=a["tables"][: n * self.max_blocks].reshape(n, self.max_blocks).copy(),
+                    input_tokens=a["tokens"][: b.total_q].copy(),
+                    copies=[(int(a["copies"][2 * i]), int(a["copies"][2 * i + 1])) for i in range(b.num_copies)],
+                    preempted=[int(x) for x in a["preempted"][: b.num_preempted]],
+                    total_q=b.total_q, max_q_len=b.max_q_len, max_context_len=b.max_context_len)
+
+    def commit(self, next_tokens, finished=None) -> None:
+        n = len(next_tokens)
+        toks = (ctypes.c_int32 * max(n, 1))(*[int(t) for t in next_tokens])
+        fin = None if finished is None else (ctypes.c_uint8 * max(n, 1))(*[1 if f else 0 for f in finished])
+        _check("pa_sched_commit", lib().pa_sched_commit(self._h, toks, fin, n))
+
+    def stats(self):
+        """(waiting, running, finished, preemptions)."""
+        w, r = ctypes.c_int32(0), ctypes.c_int32(0)
+        f, p = ctypes.c_int64(0), ctypes.c_int64(0)
+        _check("pa_sched_stats", lib().pa_sched_stats(self._h, ctypes.byref(w), ctypes.byref(r), ctypes.byref(f),
+                                                      ctypes.byref(p)))
+        return w.value, r.value, f.value, p.value

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
-SOURCES = ["api.cpp", "block_manager.cpp", "cache_write.hip", "decode.hip", "varlen.hip", "multiquery.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "scheduler.cpp", "cache_write.hip", "decode.hip", "varlen.hip", "multiquery.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -284,3 +284,8 @@ pa_status_t pa_bm_stats(const pa_block_manager* m, int32_t* free_blocks, int32_t
 }
 
 }  // extern "C"
+
+namespace pa {
+int32_t bm_block_size(const pa_block_manager* m) { return m->block_size; }
+int32_t bm_num_blocks(const pa_block_manager* m) { return m->num_blocks; }
+}  // namespace pa
