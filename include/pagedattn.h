@@ -289,7 +289,8 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
  * it); rows of sequences with n_s >= 2 through MFMA: when max_q_len * gqa_group <= 32 (a few
  * tokens per sequence, e.g. draft tokens of speculative decoding) one pass over each context
  * serves all its rows, otherwise 128-row query tiles.  When total_q = num_seqs * max_q_len and
- * max_q_len >= 2 no sequence has a single row and the decode kernel is not launched.
+ * max_q_len >= 2 no sequence has a single row and the decode kernel is not launched; when
+ * max_q_len <= 1 only the decode kernel is.
  * Supported: bf16 query and cache.  A row whose position is negative (n_s > L) sees no key and
  * comes out zero.
  */

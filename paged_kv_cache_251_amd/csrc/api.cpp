@@ -423,7 +423,7 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
     e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
     if (e == hipSuccess) e = pa::launch_decode_reduce(p, true, head_dim, num_kv_heads * gqa_group, num_seqs, stream);
   }
-  if (e == hipSuccess) {
+  if (e == hipSuccess && max_q_len >= 2) {  // some sequence may have several rows
     if (pa::multiquery_applies(gqa_group, max_q_len))
       e = pa::launch_varlen_multiquery(p, head_dim, gqa_group, num_seqs, max_q_len, stream);
     else
