@@ -343,7 +343,7 @@ def bench_multi_token(args, batches, timed, call, step, np):
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(step_bytes),
         "roofline": {
-            "kernel": "varlen_prefill_kernel (every row; no decode launch)",
+            "kernel": "varlen_multiquery_kernel (every row; no decode launch)",
             "bound": "hbm",
             "achieved": round(call_gbs, 2),
             "peak": HBM_PEAK_GBS,
