@@ -539,15 +539,17 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
 }
 
 // Merge the partitions of every (sequence, query head) that was split: M = max_j m_j,
-// w_j = 2^(m_j - M) l_j, out = sum_j w_j o_j / sum_j w_j.  256 threads: four groups of 64
-// lanes take every fourth partition (each lane D/64 dims), then combine through LDS.
+// w_j = 2^(m_j - M) l_j, out = sum_j w_j o_j / sum_j w_j.  256 threads: NG groups of D/4
+// lanes take every NG-th partition, each lane 4 dims (one 16-byte load per partition row), with
+// the loop unrolled so that several partitions' loads are in flight; the groups then combine
+// through LDS.
 template <int D, bool OUT_BF16>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p) {
-  constexpr int PER = D / 64;
-  constexpr int NG = 4;
+  constexpr int LPR = D / 4;     // lanes per partition row
+  constexpr int NG = 256 / LPR;  // partition groups
   const int h = blockIdx.x, s = blockIdx.y;
   const int hq = gridDim.x;
-  const int lane = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int sub = threadIdx.x % LPR, grp = threadIdx.x / LPR;
   int qrow = s;
   if (p.cu_q != nullptr) {
     const int a = load_invariant(p.cu_q + s), b = load_invariant(p.cu_q + s + 1);
@@ -561,44 +563,57 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p
   const int nparts = (L + p.partition_tokens - 1) / p.partition_tokens;
   if (nparts <= 1) return;
   const size_t base = ((size_t)s * hq + h) * p.max_parts;
-  __shared__ float sm_red[NG];
-  __shared__ float sm_num[NG][D];
+  __shared__ float sm_red[4];
+  __shared__ float sm_den[NG];
+  __shared__ float4 sm_num[NG][LPR];
 
   float mx = -__builtin_inff();
-  for (int j = threadIdx.x; j < nparts; j += 64 * NG) mx = fmaxf(mx, p.ws_m[base + j]);
+  for (int j = threadIdx.x; j < nparts; j += 256) mx = fmaxf(mx, p.ws_m[base + j]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) sm_red[grp] = mx;
+  if ((threadIdx.x & 63) == 0) sm_red[threadIdx.x >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
 
   float den = 0.f;
-  float num[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) num[e] = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4* wo = reinterpret_cast<const float4*>(p.ws_o);
+#pragma unroll 4
   for (int j = grp; j < nparts; j += NG) {
     const float mj = p.ws_m[base + j];
     const float w = (mj == -__builtin_inff()) ? 0.f : fast_exp2(mj - mx) * p.ws_l[base + j];
+    const float4 o = wo[(base + j) * LPR + sub];
     den += w;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) num[e] = fmaf(w, p.ws_o[(base + j) * D + lane + 64 * e], num[e]);
+    num.x = fmaf(w, o.x, num.x);
+    num.y = fmaf(w, o.y, num.y);
+    num.z = fmaf(w, o.z, num.z);
+    num.w = fmaf(w, o.w, num.w);
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) sm_num[grp][lane + 64 * e] = num[e];
-  __syncthreads();  // sm_red is read above by every thread before it is rewritten here
-  if (lane == 0) sm_red[grp] = den;
+  sm_num[grp][sub] = num;
+  if (sub == 0) sm_den[grp] = den;
   __syncthreads();
-  if (grp != 0) return;
-  den = sm_red[0] + sm_red[1] + sm_red[2] + sm_red[3];
-  const size_t orow = ((size_t)qrow * hq + h) * D;
+  if (threadIdx.x >= LPR) return;
+  float4 t = sm_num[0][sub];
+  float dsum = sm_den[0];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int d = lane + 64 * e;
-    const float o = den > 0.f ? (sm_num[0][d] + sm_num[1][d] + sm_num[2][d] + sm_num[3][d]) / den : 0.f;
-    if constexpr (OUT_BF16)
-      reinterpret_cast<uint16_t*>(p.out)[orow + d] = (uint16_t)f32_to_bf16_rne(o);
-    else
-      reinterpret_cast<float*>(p.out)[orow + d] = o;
+  for (int g = 1; g < NG; ++g) {
+    const float4 v = sm_num[g][sub];
+    t.x += v.x;
+    t.y += v.y;
+    t.z += v.z;
+    t.w += v.w;
+    dsum += sm_den[g];
+  }
+  const float o4[4] = {dsum > 0.f ? t.x / dsum : 0.f, dsum > 0.f ? t.y / dsum : 0.f, dsum > 0.f ? t.z / dsum : 0.f,
+                       dsum > 0.f ? t.w / dsum : 0.f};
+  const size_t orow = ((size_t)qrow * hq + h) * D + (size_t)sub * 4;
+  if constexpr (OUT_BF16) {
+    uint2 w2;
+    w2.x = f32_to_bf16_rne(o4[0]) | (f32_to_bf16_rne(o4[1]) << 16);
+    w2.y = f32_to_bf16_rne(o4[2]) | (f32_to_bf16_rne(o4[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + orow) = w2;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + orow) = make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
 }
 
