@@ -16,13 +16,17 @@ from .reference import (  # noqa: F401
     cache_write,
     combine_partials,
     decode_storage,
+    dequantize_e4m3,
     dequantize_int8,
+    e4m3_to_f64,
     e5m2_to_f64,
+    f64_to_e4m3,
     f64_to_e5m2,
     gather_kv,
     new_pool,
     paged_decode,
     paged_varlen,
+    quantize_e4m3,
     quantize_int8,
     slot_mapping,
 )

@@ -29,7 +29,8 @@ What the pages fix, restated:
   * Low-bit KV caches save memory and traffic in a memory-bound step [OPT 2.6];
     an INT8 KV cache is one such format [FW: frameworks page, LMDeploy: KV Cache
     INT8].  No page fixes a scheme, so ``quantize_int8`` states the library's:
-    symmetric, one float32 scale per (token, KV head) row.
+    symmetric, one float32 scale per (token, KV head) row.  ``quantize_e4m3`` is the same
+    per-row scaling onto the FP8 E4M3 format's range (the "scaled FP8" variant).
 
 Storage conventions: raw bits as in device memory -- f32 as float32, bf16 as
 uint16 patterns, e5m2 as uint8 codes.  The oracle's own pool layout is
@@ -134,6 +135,64 @@ def quantize_int8(x) -> tuple[np.ndarray, np.ndarray]:
 def dequantize_int8(codes, scales) -> np.ndarray:
     """code * scale in float64 (exact: an 8-bit integer times a float32)."""
     return np.asarray(codes, np.float64) * np.asarray(scales, np.float64)[..., None]
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 rows with a scale  [OPT 2.6; the scheme is this library's]
+# --------------------------------------------------------------------------
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Value of an E4M3 code (OCP "FN" variant: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 is subnormal, no infinities, S.1111.111 is NaN, largest finite 448)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = c >> 7
+    e = (c >> 3) & 15
+    m = c & 7
+    sign = np.where(s == 1, -1.0, 1.0)
+    val = np.where(e == 0, (m / 8.0) * 2.0**-6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+# Finite non-negative E4M3 magnitudes in code order 0x00..0x7E (ascending).
+_E4M3_LADDER = e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+
+
+def f64_to_e4m3(x) -> np.ndarray:
+    """Round to the nearest E4M3 value, ties to the even code, saturating: a magnitude at or
+    above the largest finite value (448) gives 448.  NaN gives 0x7F (sign dropped)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    sign = (np.signbit(x).astype(np.uint8) << np.uint8(7)).astype(np.uint8)
+    hi = np.clip(np.searchsorted(_E4M3_LADDER, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - _E4M3_LADDER[lo]
+    d_hi = _E4M3_LADDER[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo)
+    code = np.where(a >= 448.0, 0x7E, code).astype(np.uint8) | sign
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_e4m3(x) -> tuple[np.ndarray, np.ndarray]:
+    """E4M3 codes of every row (last axis) scaled to the format's range, and one float32 scale
+    per row.  In float32 arithmetic (IEEE, round to nearest even):
+        amax  = max |x|            (maxNum: a NaN element is ignored)
+        inv   = 448 / amax         (0 when amax is 0 or NaN)
+        code  = f64_to_e4m3(x * inv)   (the float32 product, rounded to E4M3 exactly once)
+        scale = amax / 448
+    The dequantised value is e4m3_to_f64(code) * scale."""
+    x32 = np.asarray(x, dtype=np.float32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        amax = np.fmax.reduce(np.abs(x32), axis=-1)
+        inv = np.where(amax > 0, np.float32(448) / amax, np.float32(0)).astype(np.float32)
+        prod = (x32 * inv[..., None]).astype(np.float32)
+        scale = (amax / np.float32(448)).astype(np.float32)
+    return f64_to_e4m3(prod.astype(np.float64)), scale
+
+
+def dequantize_e4m3(codes, scales) -> np.ndarray:
+    """E4M3 value * scale in float64 (exact)."""
+    return e4m3_to_f64(codes) * np.asarray(scales, np.float64)[..., None]
 
 
 # --------------------------------------------------------------------------
