@@ -30,13 +30,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: KV-read HBM GB/s (% of peak) + seq-steps/sec, 1 GPU"
 HBM_PEAK_GBS = 8000.0
-KV_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1, "int8": 1}
+KV_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1, "int8": 1, "e4m3": 1}
+SCALED = ("int8", "e4m3")  # pools with a float32 scale per (token, KV head) row
 
 
 def row_bytes(w) -> int:
     """Pool bytes of one (token, KV head) row: head_dim elements, plus the float32 scale of an
     INT8 row."""
-    return w.head_dim * KV_BYTES[w.kv_dtype] + (4 if w.kv_dtype == "int8" else 0)
+    return w.head_dim * KV_BYTES[w.kv_dtype] + (4 if w.kv_dtype in SCALED else 0)
 
 
 def parse():
@@ -45,7 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload 1-7 (1-4 decode, 5 packed prefill + decode, 6 speculative verification of 4 tokens, "
-                    "7 decode over an INT8 pool)")
+                    "7 decode over an INT8 pool, 8 over a scaled FP8 E4M3 pool)")
     ap.add_argument("--replicas", type=int, default=0, help="resident batches to rotate (0: enough for >= 1.2 GB)")
     ap.add_argument("--partition", type=int, default=None, help="partition tokens (default: workload's, else auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
@@ -82,16 +83,17 @@ class Batch:
         self.w = w
         self.tables = torch.from_numpy(w.block_tables).to(dev)
         self.lens = torch.from_numpy(w.context_lens).to(dev)
-        if w.kv_dtype == "int8":  # codes, then 16 float32 scales per (block, head); every word NaN
+        if w.kv_dtype in SCALED:  # codes, then 16 float32 scales per (block, head); every word NaN
             words = (w.num_blocks, w.num_kv_heads, (w.block_size * w.head_dim + 64) // 4)
-            self.pk = torch.full(words, POISON_BITS["int8"], dtype=torch.int32, device=dev).view(torch.int8)
+            store = torch.int8 if w.kv_dtype == "int8" else torch.float8_e4m3fn
+            self.pk = torch.full(words, POISON_BITS[w.kv_dtype], dtype=torch.int32, device=dev).view(store)
         else:
             shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
             ints = {"f32": torch.int32, "bf16": torch.int16, "e5m2": torch.uint8}[w.kv_dtype]
             store = {"f32": torch.float32, "bf16": torch.bfloat16, "e5m2": torch.uint8}[w.kv_dtype]
             self.pk = torch.full(shape, POISON_BITS[w.kv_dtype], dtype=ints, device=dev).view(store)
-        # an INT8 pool is written by the cache write's quantiser (no fused append)
-        self.fused = w.kv_dtype != "int8"
+        # a scaled pool is written by the cache write's quantiser (no fused append)
+        self.fused = w.kv_dtype not in SCALED
         self.pv = self.pk.clone()
         hist = write_plan(w, "cached")
         slots = pa.slot_mapping(torch.from_numpy(hist.cu).to(dev), torch.from_numpy(hist.end_pos).to(dev),
@@ -489,7 +491,8 @@ def main():
             "partition_tokens": batches[0].resolved,
             "resident_batches": reps,
             "step": ("one launch: slot mapping + cache write of the newest token + decode attention" if fused else
-                     "slot mapping + INT8 cache write (quantise) of the newest token + decode attention") +
+                     f"slot mapping + {w0.kv_dtype.upper()} cache write (quantise) of the newest token + decode "
+                     "attention") +
                     (" (split-KV partitions) + the separate reduce kernel" if batches[0].split else ""),
         },
         "seq_steps_per_s": round(seqs / (ms_step * 1e-3), 1),
@@ -502,7 +505,7 @@ def main():
                      (" + separate reduce kernel" if batches[0].split else "")},
         "wall_s": round(wall, 4),
         "roofline": {
-            "kernel": "decode_partition_kernel" + (" (append mode)" if fused else " (INT8 pool)"),
+            "kernel": "decode_partition_kernel" + (" (append mode)" if fused else f" ({w0.kv_dtype.upper()} pool)"),
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -561,8 +564,8 @@ def cpu_baseline(w, budget_s):
         while t_used < budget_s:
             sel = [(s0 + i) % w.num_seqs for i in range(8)]
             # history of these sequences (not timed: it is the state the step starts from)
-            int8 = w.kv_dtype == "int8"
-            if int8:  # the oracle's INT8 pool: dequantised rows (code * scale), float64
+            scaled = w.kv_dtype in SCALED
+            if scaled:  # the oracle's scaled pool: dequantised rows (code value * scale), float64
                 pk = np.full((w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim), np.nan)
             else:
                 pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
@@ -570,11 +573,12 @@ def cpu_baseline(w, budget_s):
             pv = pk.copy()
 
             def write(pool, rows, slots):
-                if int8:
-                    codes, scales = oracle.quantize_int8(oracle.decode_storage(rows, w.src_dtype).astype(np.float32))
+                if scaled:
+                    quant, dequant = ((oracle.quantize_int8, oracle.dequantize_int8) if w.kv_dtype == "int8" else
+                                      (oracle.quantize_e4m3, oracle.dequantize_e4m3))
+                    codes, scales = quant(oracle.decode_storage(rows, w.src_dtype).astype(np.float32))
                     keep = slots >= 0
-                    pool[slots[keep] // w.block_size, slots[keep] % w.block_size] = \
-                        oracle.dequantize_int8(codes[keep], scales[keep])
+                    pool[slots[keep] // w.block_size, slots[keep] % w.block_size] = dequant(codes[keep], scales[keep])
                 else:
                     oracle.cache_write(pool, rows, slots, w.src_dtype, w.kv_dtype, w.block_size)
 
@@ -587,7 +591,7 @@ def cpu_baseline(w, budget_s):
             ns = oracle.slot_mapping(w.block_tables, new.counts, new.end_pos, w.block_size)
             write(pk, new.k, ns)
             write(pv, new.v, ns)
-            oracle.paged_decode(pk, pv, "f64" if int8 else w.kv_dtype, q, w.q_dtype, w.block_tables,
+            oracle.paged_decode(pk, pv, "f64" if scaled else w.kv_dtype, q, w.q_dtype, w.block_tables,
                                 w.context_lens, w.block_size, w.scale, seqs=sel)
             t_used += time.perf_counter() - t0
             done_seqs += len(sel)

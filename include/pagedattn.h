@@ -49,6 +49,15 @@
  *            probability times the value scale in f16 (11 significant bits; p <= 256 with
  *            the kernel's lazy running max): value rows need amax below 32000, and
  *            products below 2^-14 keep only f16's subnormal precision.
+ *   PA_FP8_E4M3  scaled FP8: OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ *            bits, no infinities, largest finite 448, S.1111.111 = NaN) of each (token, KV head)
+ *            row scaled to the format's range, with one float32 scale per row [OPT 2.6; the
+ *            scheme is this library's].  The cache write computes, in float32: amax as for
+ *            INT8, inv = amax > 0 ? 448 / amax : 0, code_d = x_d * inv rounded to the nearest
+ *            E4M3 value (ties to the even code, saturating at 448; a NaN product gives 0x7F),
+ *            scale = amax / 448; a reader uses value(code) * scale.  Pool layout as for INT8.
+ *            Decode widens codes to f16 exactly and applies the scales as for INT8 (value rows
+ *            need amax below 114000 for the f16 weights).
  *
  * Conventions for every entry point
  *   - All pointers are device pointers unless stated; the caller owns every buffer.
@@ -66,8 +75,8 @@
  *     [0, min(max_context_len, max_blocks_per_seq * block_size)].  Results for such
  *     inputs are unspecified but no access leaves the buffers described here.
  *   - Supported now: block_size 16; head_dim 64 or 128; gqa_group 1, 2, 4, 8 or 16;
- *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), and (BF16, INT8)
- *     for the decode calls without append.
+ *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), and (BF16, INT8) and
+ *     (BF16, FP8_E4M3) for the decode calls without append.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -81,7 +90,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum {
   PA_OK = 0,
@@ -92,7 +101,7 @@ typedef enum {
   PA_ERR_OUT_OF_BLOCKS = 5
 } pa_status_t;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E5M2 = 2, PA_INT8 = 3 } pa_dtype_t;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E5M2 = 2, PA_INT8 = 3, PA_FP8_E4M3 = 4 } pa_dtype_t;
 
 /* Version of this header's ABI (PA_ABI_VERSION). */
 int pa_abi_version(void);
@@ -140,10 +149,10 @@ pa_status_t paged_kv_slot_mapping(int32_t* slot_mapping, const int32_t* cu_token
  *   value_cache   [num_blocks][num_kv_heads][block_size][head_dim] of cache_dtype
  *   slot_mapping  int32 [num_tokens]; row r goes to block slot/block_size, offset
  *                 slot % block_size; slot < 0 or >= num_blocks*block_size skips the row
- *   (src, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, INT8)}; a same-type
- *   write copies bits, the E5M2 cast is round-to-nearest-even, an INT8 write quantises each
- *   (token, KV head) row and stores its codes and scale (see above; block_size 16 and
- *   head_dim 64 or 128 for INT8).
+ *   (src, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, INT8), (BF16,
+ *   FP8_E4M3)}; a same-type write copies bits, the E5M2 cast is round-to-nearest-even, an INT8
+ *   or FP8_E4M3 write quantises each (token, KV head) row and stores its codes and scale (see
+ *   above; block_size 16 and head_dim 64 or 128 for these).
  *   Two rows with the same slot in one call race: the stored row is unspecified.
  */
 pa_status_t kv_cache_write(const void* key, const void* value, void* key_cache,
@@ -251,8 +260,8 @@ pa_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens
  * paged_attention_decode over all L tokens.  The result is bit-identical to
  * paged_kv_slot_mapping + kv_cache_write + paged_attention_decode with the same
  * partition size.  A sequence with L = 0 appends nothing.  A slot whose table entry is
- * outside [0, num_blocks) is not written.  An INT8 pool is not supported here
- * (PA_ERR_UNSUPPORTED): write its rows with kv_cache_write.
+ * outside [0, num_blocks) is not written.  INT8 and FP8_E4M3 pools are not supported here
+ * (PA_ERR_UNSUPPORTED): write their rows with kv_cache_write.
  *
  * flags: PA_APPEND_SKIP_REDUCE -- run only the streaming pass; the caller then runs
  *        paged_attention_decode_reduce (same arguments) when a sequence is split.
@@ -381,8 +390,7 @@ pa_status_t pa_bm_stats(const pa_block_manager* manager, int32_t* free_blocks, i
  * pairs[2i] -> block pairs[2i+1] (every KV head, every slot).  Carries out the copies that
  * pa_bm_append reports.  pairs: device int32 [2 * num_pairs]; a pair with an entry outside
  * [0, num_blocks) or src == dst is skipped; two pairs with the same destination race.
- * cache_dtype: PA_F32, PA_BF16, PA_FP8_E5M2 or PA_INT8 (bytes are copied; an INT8 block
- * carries its scales).
+ * cache_dtype: any pool type (bytes are copied; an INT8 or FP8_E4M3 block carries its scales).
  */
 pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,

@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     PA_BF16,
     PA_F32,
+    PA_FP8_E4M3,
     PA_FP8_E5M2,
     PA_INT8,
     BlockManager,

@@ -16,8 +16,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
-PA_F32, PA_BF16, PA_FP8_E5M2, PA_INT8 = 0, 1, 2, 3
-INT8_BLOCK = 16  # tokens per block of an INT8 pool
+PA_F32, PA_BF16, PA_FP8_E5M2, PA_INT8, PA_FP8_E4M3 = 0, 1, 2, 3, 4
+INT8_BLOCK = 16  # tokens per block of a scaled (INT8 / FP8_E4M3) pool
+# torch element types that carry the bytes of a scaled pool: [nb, Hkv, 16 * D + 64]
+SCALED_POOL_TYPES = {torch.int8: PA_INT8, torch.float8_e4m3fn: PA_FP8_E4M3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "device error",
           5: "out of blocks"}
 PA_ERR_OUT_OF_BLOCKS = 5
@@ -146,33 +148,39 @@ def dtype_code(t: torch.Tensor) -> int:
         return PA_BF16
     if t.dtype in (torch.uint8, torch.float8_e5m2):
         return PA_FP8_E5M2
-    if t.dtype == torch.int8:
-        return PA_INT8
+    if t.dtype in SCALED_POOL_TYPES:
+        return SCALED_POOL_TYPES[t.dtype]
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
 def _pool_dims(cache: torch.Tensor):
     """(num_blocks, num_kv_heads, block_size, head_dim) of a pool: [nb, Hkv, B, D] of its element
-    type, or for INT8 int8 bytes [nb, Hkv, 16 * D + 64] (codes, then 16 float32 scales)."""
-    if cache.dtype == torch.int8:
+    type, or for a scaled pool (torch.int8: INT8 codes, torch.float8_e4m3fn: E4M3 codes) bytes
+    [nb, Hkv, 16 * D + 64] (codes, then 16 float32 scales)."""
+    if cache.dtype in SCALED_POOL_TYPES:
         _expect(cache.dim() == 3 and (cache.shape[2] - 64) % INT8_BLOCK == 0 and cache.shape[2] > 64,
-                "an INT8 pool is int8 [num_blocks, Hkv, 16 * D + 64]")
+                "a scaled pool is [num_blocks, Hkv, 16 * D + 64] bytes")
         return cache.shape[0], cache.shape[1], INT8_BLOCK, (cache.shape[2] - 64) // INT8_BLOCK
     _expect(cache.dim() == 4, "a pool is [num_blocks, Hkv, block_size, D]")
     return tuple(cache.shape)
 
 
-def new_int8_pool(num_blocks: int, num_kv_heads: int, head_dim: int, device) -> torch.Tensor:
-    """Zeroed INT8 pool (codes and scales) for num_blocks blocks of 16 tokens."""
-    return torch.zeros((num_blocks, num_kv_heads, INT8_BLOCK * head_dim + 64), dtype=torch.int8, device=device)
+def new_int8_pool(num_blocks: int, num_kv_heads: int, head_dim: int, device,
+                  dtype: torch.dtype = torch.int8) -> torch.Tensor:
+    """Zeroed scaled pool (codes and scales) for num_blocks blocks of 16 tokens; dtype torch.int8
+    (INT8 codes) or torch.float8_e4m3fn (FP8 E4M3 codes)."""
+    _expect(dtype in SCALED_POOL_TYPES, "a scaled pool is torch.int8 or torch.float8_e4m3fn")
+    return torch.zeros((num_blocks, num_kv_heads, INT8_BLOCK * head_dim + 64), dtype=torch.int8,
+                       device=device).view(dtype)
 
 
 def int8_pool_split(pool: torch.Tensor):
-    """Views of an INT8 pool: codes [nb, Hkv, 16, D] (int8) and the scales [nb, Hkv, 16] (float32)
-    in their stored order -- the scale of token t at index 4 * (t % 4) + t // 4."""
+    """Views of a scaled pool: codes [nb, Hkv, 16, D] (the pool's type) and the scales
+    [nb, Hkv, 16] (float32) in their stored order -- the scale of token t at index
+    4 * (t % 4) + t // 4."""
     nb, hkv, bs, d = _pool_dims(pool)
     codes = pool[:, :, : bs * d].view(nb, hkv, bs, d)
-    scales = pool[:, :, bs * d:].view(torch.float32)
+    scales = pool.view(torch.int8)[:, :, bs * d:].view(torch.float32)
     return codes, scales
 
 

@@ -46,10 +46,22 @@ pa_status_t device_status(hipError_t e, const char* what) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int kv_kind(pa_dtype_t t) {
-  return t == PA_F32 ? pa::KV_F32 : t == PA_BF16 ? pa::KV_BF16 : t == PA_FP8_E5M2 ? pa::KV_E5M2 : pa::KV_I8;
+  switch (t) {
+    case PA_F32: return pa::KV_F32;
+    case PA_BF16: return pa::KV_BF16;
+    case PA_FP8_E5M2: return pa::KV_E5M2;
+    case PA_INT8: return pa::KV_I8;
+    case PA_FP8_E4M3: return pa::KV_E4M3;
+  }
+  return -1;
 }
 
-bool valid_dtype(int t) { return t == PA_F32 || t == PA_BF16 || t == PA_FP8_E5M2 || t == PA_INT8; }
+bool valid_dtype(int t) {
+  return t == PA_F32 || t == PA_BF16 || t == PA_FP8_E5M2 || t == PA_INT8 || t == PA_FP8_E4M3;
+}
+
+// Pools with one float32 scale per (token, KV head) after each tile's codes.
+bool scaled_dtype(int t) { return t == PA_INT8 || t == PA_FP8_E4M3; }
 
 constexpr int64_t kMaxGridYZ = 65535;
 
@@ -123,7 +135,7 @@ pa_status_t check_attention(const char* fn, int32_t num_seqs, int32_t num_kv_hea
     return fail(PA_ERR_INVALID_ARGUMENT, "%s: unknown dtype (q %d, kv %d)", fn, (int)q_dtype, (int)kv_dtype);
   const bool pair_ok = (q_dtype == PA_F32 && kv_dtype == PA_F32) || (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
                        (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E5M2) ||
-                       (q_dtype == PA_BF16 && kv_dtype == PA_INT8);
+                       (q_dtype == PA_BF16 && scaled_dtype(kv_dtype));
   if (!pair_ok)
     return fail(PA_ERR_UNSUPPORTED, "%s: (q, kv) dtype pair (%d, %d) not supported", fn, (int)q_dtype,
                 (int)kv_dtype);
@@ -196,12 +208,12 @@ pa_status_t kv_cache_write(const void* key, const void* value, void* key_cache, 
   const bool pair_ok = (src_dtype == PA_F32 && cache_dtype == PA_F32) ||
                        (src_dtype == PA_BF16 && cache_dtype == PA_BF16) ||
                        (src_dtype == PA_BF16 && cache_dtype == PA_FP8_E5M2) ||
-                       (src_dtype == PA_BF16 && cache_dtype == PA_INT8);
+                       (src_dtype == PA_BF16 && scaled_dtype(cache_dtype));
   if (!pair_ok)
     return fail(PA_ERR_UNSUPPORTED, "%s: (src, cache) dtype pair (%d, %d) not supported", fn, (int)src_dtype,
                 (int)cache_dtype);
-  if (cache_dtype == PA_INT8 && (block_size != 16 || (head_dim != 64 && head_dim != 128)))
-    return fail(PA_ERR_UNSUPPORTED, "%s: an INT8 pool takes block_size 16 and head_dim 64 or 128", fn);
+  if (scaled_dtype(cache_dtype) && (block_size != 16 || (head_dim != 64 && head_dim != 128)))
+    return fail(PA_ERR_UNSUPPORTED, "%s: an INT8 / FP8_E4M3 pool takes block_size 16 and head_dim 64 or 128", fn);
   const int src_sz = src_dtype == PA_F32 ? 4 : 2;
   if ((static_cast<int64_t>(head_dim) * src_sz) % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d rows are not a multiple of 16 bytes", fn, head_dim);
@@ -372,8 +384,8 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
                                   max_context_len, scale, q_dtype, kv_dtype, partition_size, workspace,
                                   workspace_bytes, true);
   if (st != PA_OK) return st;
-  if (kv_dtype == PA_INT8)
-    return fail(PA_ERR_UNSUPPORTED, "%s: INT8 pools are written by kv_cache_write (no fused append)", fn);
+  if (scaled_dtype(kv_dtype))
+    return fail(PA_ERR_UNSUPPORTED, "%s: INT8 / FP8_E4M3 pools are written by kv_cache_write (no fused append)", fn);
   if (num_seqs == 0) return ok();
   if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "%s: null key/value row pointer", fn);
   if (!aligned(key, 16) || !aligned(value, 16))
@@ -440,11 +452,11 @@ pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32
   if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
     return fail(PA_ERR_INVALID_ARGUMENT, "%s: num_kv_heads, head_dim, block_size and num_blocks must be > 0", fn);
   if (!valid_dtype(cache_dtype)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: unknown cache dtype %d", fn, (int)cache_dtype);
-  if (cache_dtype == PA_INT8 && block_size != 16)
-    return fail(PA_ERR_UNSUPPORTED, "%s: an INT8 pool takes block_size 16", fn);
+  if (scaled_dtype(cache_dtype) && block_size != 16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: an INT8 / FP8_E4M3 pool takes block_size 16", fn);
   const size_t elem = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
-  // an INT8 tile carries one float32 scale per token after its codes
-  const size_t row_bytes = static_cast<size_t>(head_dim) * elem + (cache_dtype == PA_INT8 ? 4 : 0);
+  // a scaled tile carries one float32 scale per token after its codes
+  const size_t row_bytes = static_cast<size_t>(head_dim) * elem + (scaled_dtype(cache_dtype) ? 4 : 0);
   const size_t block_bytes = static_cast<size_t>(num_kv_heads) * block_size * row_bytes;
   if (block_bytes % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: a block of %zu bytes is not a multiple of 16", fn, block_bytes);
   if (num_pairs == 0) return ok();

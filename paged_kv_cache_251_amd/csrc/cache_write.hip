@@ -3,8 +3,9 @@
 // Colossal-Inference release post, "分块式KV缓存 (BlockedKeyValueCache)": logical blocks map
 // through a block table to physical blocks anywhere in the pool; "KV缓存量化 (KVCache
 // Quant)": the kernel that stores new keys and values casts them to FP8 E5M2 on the way.
-// LLM inference frameworks overview, "LMDeploy": an INT8 KV cache; the scheme (symmetric codes,
-// one float32 scale per (token, KV head) row) is this library's.
+// LLM inference frameworks overview, "LMDeploy": an INT8 KV cache; LLM inference optimisation
+// overview, 2.6: low-bit caches.  The schemes (INT8 codes or FP8 E4M3 codes, one float32 scale
+// per (token, KV head) row) are this library's.
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
 
@@ -92,20 +93,23 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint4* __restric
   }
 }
 
-// bf16 rows -> INT8 pool.  D/8 consecutive lanes take one (token, KV head) row, 8 elements each
-// (one 16-byte load); the row's amax is reduced across them, then every lane stores its 8 codes
-// and the row's first lane the scale.  The maximum is taken on the bf16 magnitude patterns as
-// integers (order-preserving for non-NaN values; NaN mapped below every number), so NaN
-// elements are ignored whatever their payload and an all-NaN row gets a NaN amax.
-template <int D>
-__global__ __launch_bounds__(256) void cache_write_i8_kernel(const uint4* __restrict__ key,
+// bf16 rows -> scaled 8-bit pool (KV_I8: codes in [-127, 127], scale amax / 127; KV_E4M3: FP8
+// E4M3 codes of x * 448 / amax, scale amax / 448).  D/8 consecutive lanes take one (token, KV
+// head) row, 8 elements each (one 16-byte load); the row's amax is reduced across them, then
+// every lane stores its 8 codes and the row's first lane the scale.  The maximum is taken on
+// the bf16 magnitude patterns as integers (order-preserving for non-NaN values; NaN mapped
+// below every number), so NaN elements are ignored whatever their payload and an all-NaN row
+// gets a NaN amax.
+template <int D, int KV>
+__global__ __launch_bounds__(256) void cache_write_q8_kernel(const uint4* __restrict__ key,
                                                              const uint4* __restrict__ value,
                                                              uint8_t* __restrict__ key_cache,
                                                              uint8_t* __restrict__ value_cache,
                                                              const int32_t* __restrict__ slots, int32_t num_tokens,
                                                              int32_t num_kv_heads, int32_t num_blocks) {
   constexpr int LPR = D / 8;  // lanes per row; divides 64, so a row never straddles waves
-  constexpr int TILE = TileStride<KV_I8, D>::value;
+  constexpr int TILE = TileStride<KV, D>::value;
+  constexpr float RANGE = KV == KV_I8 ? 127.0f : 448.0f;  // largest code magnitude
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)num_tokens * num_kv_heads * LPR;
   if (i >= total) return;  // total is a multiple of LPR: a row's lanes leave together
@@ -131,16 +135,21 @@ __global__ __launch_bounds__(256) void cache_write_i8_kernel(const uint4* __rest
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) key_max = max(key_max, __shfl_xor(key_max, off));
     const float amax = key_max < 0 ? __builtin_nanf("") : as_f32((uint32_t)key_max << 16);
-    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    const float inv = amax > 0.f ? RANGE / amax : 0.f;
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float q = rintf(x[k] * inv);
-      const int code = q != q ? -127 : (int)fminf(fmaxf(q, -127.f), 127.f);
-      packed[k >> 2] |= ((uint32_t)code & 0xFFu) << (8 * (k & 3));
+      uint32_t code;
+      if constexpr (KV == KV_I8) {
+        const float q = rintf(x[k] * inv);
+        code = (uint32_t)(q != q ? -127 : (int)fminf(fmaxf(q, -127.f), 127.f)) & 0xFFu;
+      } else {
+        code = f32_to_e4m3_sat(x[k] * inv);
+      }
+      packed[k >> 2] |= code << (8 * (k & 3));
     }
     *reinterpret_cast<uint2*>(pool + tile + (size_t)r * D + (size_t)c * 8) = make_uint2(packed[0], packed[1]);
-    if (c == 0) *reinterpret_cast<float*>(pool + tile + 16 * D + 4 * (4 * (r & 3) + (r >> 2))) = amax / 127.0f;
+    if (c == 0) *reinterpret_cast<float*>(pool + tile + 16 * D + 4 * (4 * (r & 3) + (r >> 2))) = amax / RANGE;
   };
   quantize(key[i], key_cache);
   quantize(value[i], value_cache);
@@ -168,11 +177,17 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
     hipLaunchKernelGGL((cache_write_kernel<KV_BF16, KV_E5M2>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
                        slots, num_tokens, num_kv_heads, head_dim, block_size, num_blocks);
   else if (src_kind == KV_BF16 && cache_kind == KV_I8 && block_size == 16 && head_dim == 128)
-    hipLaunchKernelGGL((cache_write_i8_kernel<128>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc, slots,
-                       num_tokens, num_kv_heads, num_blocks);
+    hipLaunchKernelGGL((cache_write_q8_kernel<128, KV_I8>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
+                       slots, num_tokens, num_kv_heads, num_blocks);
   else if (src_kind == KV_BF16 && cache_kind == KV_I8 && block_size == 16 && head_dim == 64)
-    hipLaunchKernelGGL((cache_write_i8_kernel<64>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc, slots,
-                       num_tokens, num_kv_heads, num_blocks);
+    hipLaunchKernelGGL((cache_write_q8_kernel<64, KV_I8>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
+                       slots, num_tokens, num_kv_heads, num_blocks);
+  else if (src_kind == KV_BF16 && cache_kind == KV_E4M3 && block_size == 16 && head_dim == 128)
+    hipLaunchKernelGGL((cache_write_q8_kernel<128, KV_E4M3>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
+                       slots, num_tokens, num_kv_heads, num_blocks);
+  else if (src_kind == KV_BF16 && cache_kind == KV_E4M3 && block_size == 16 && head_dim == 64)
+    hipLaunchKernelGGL((cache_write_q8_kernel<64, KV_E4M3>), dim3(blocks), dim3(256), 0, stream, k, v, kc, vc,
+                       slots, num_tokens, num_kv_heads, num_blocks);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -20,9 +20,9 @@
 //    by more than TAU (2^8): exact, since the same stale max is used for the numerator
 //    and the denominator, and it makes the rescale branch rare.
 //  * Probabilities reach the PV lanes by DPP row broadcast; V is accumulated in fp32
-//    (f32 / bf16 caches) or with f16 dot2 over token pairs (E5M2 and INT8 caches, whose
-//    codes widen exactly to f16).  An INT8 tile ends in its 16 row scales, ordered so that
-//    one 16-byte load gives a lane the scales of its row's four tokens: the key scale
+//    (f32 / bf16 caches) or with f16 dot2 over token pairs (E5M2, INT8 and E4M3 caches, whose
+//    codes widen exactly to f16).  An INT8 or E4M3 tile ends in its 16 row scales, ordered so
+//    that one 16-byte load gives a lane the scales of its row's four tokens: the key scale
 //    multiplies the finished dot product, the value scale the probability (in f16).
 //  * Rows, then waves, are merged at the end; a single partition writes the output,
 //    several write (o/l, m, l) to the workspace for the reduce kernel.
@@ -72,13 +72,14 @@ struct DecodeTile {
   static constexpr int NDW = EPL * SZ / 4;    // dwords per lane per token row
   static constexpr int NL = 4;                // loads per 16-token tile (4 rows each)
   static constexpr int QDW = KV == KV_F32 ? EPL : EPL / 2;  // q dwords per head per lane
-  static constexpr bool F16_Q = KV == KV_E5M2 || KV == KV_I8;  // bf16 query widened to f16
-  static constexpr int SCW = KV == KV_I8 ? 4 : 1;              // scale dwords per lane per tile
+  static constexpr bool F16_Q = KV == KV_E5M2 || Scaled<KV>::value;  // bf16 query widened to f16
+  static constexpr int SCW = Scaled<KV>::value ? 4 : 1;              // scale dwords per lane per tile
   static constexpr int TILE = TileStride<KV, D>::value;        // bytes per (block, KV head)
 };
 
-// The INT8 kernels with up to 4 heads per group are held to 128 VGPRs (4 waves per SIMD
-// instead of 3; the few values spilled are outside the loop); larger groups need the registers.
+// The INT8 kernels with up to 4 heads per group are held to 128 VGPRs (4 waves per SIMD instead
+// of 3; the few values spilled are outside the loop); larger groups need the registers.  The E4M3
+// kernels measured faster without the limit (they would spill more).
 #ifndef PA_I8_WAVES_PER_EU
 #define PA_I8_WAVES_PER_EU 4
 #endif
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
   // b_new then comes from the new row instead of the cache (no read-after-write inside
   // the launch).  Lane (row, col) keeps columns col*EPL .. col*EPL+EPL-1 in cache format.
   const int pos_new = L - 1;
-  const bool appending = KV != KV_I8 && p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
+  const bool appending = !Scaled<KV>::value && p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
   const int b_new = appending ? pos_new / 16 : -1;
   const int r_new = pos_new & 15;
   uint32_t knew[NDW], vnew[NDW];
@@ -249,10 +250,10 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
     const size_t off = tile + lane_off;
 #pragma unroll
     for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(kd[i], kbase + off + (size_t)i * 4 * D * SZ);
-    if constexpr (KV == KV_I8) load_dw<4, PA_NT_LOADS>(ks, kbase + tile + scale_off);
+    if constexpr (Scaled<KV>::value) load_dw<4, PA_NT_LOADS>(ks, kbase + tile + scale_off);
 #pragma unroll
     for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(vd[i], vbase + off + (size_t)i * 4 * D * SZ);
-    if constexpr (KV == KV_I8) load_dw<4, PA_NT_LOADS>(vs, vbase + tile + scale_off);
+    if constexpr (Scaled<KV>::value) load_dw<4, PA_NT_LOADS>(vs, vbase + tile + scale_off);
     __builtin_amdgcn_sched_barrier(0);  // issue the tile before any math that follows
     return ok;
   };
@@ -276,19 +277,25 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float r[G];
-      uint32_t kh[KV == KV_I8 ? 2 * NDW : 1];  // INT8 codes of this token as biased f16 pairs
-      if constexpr (KV == KV_I8) {
+      uint32_t kh[Scaled<KV>::value ? 2 * NDW : 1];  // codes of this token as f16 pairs
+      if constexpr (KV == KV_I8) {  // biased: 1152 + code
 #pragma unroll
         for (int j = 0; j < NDW; ++j) {
           const uint32_t wx = kd[i][j] ^ 0x80808080u;
           kh[2 * j] = i8_biased_lo(wx);
           kh[2 * j + 1] = i8_biased_hi(wx);
         }
+      } else if constexpr (KV == KV_E4M3) {
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) {
+          kh[2 * j] = e4m3_pair<false>(kd[i][j]);
+          kh[2 * j + 1] = e4m3_pair<true>(kd[i][j]);
+        }
       }
 #pragma unroll
       for (int k = 0; k < G; ++k) {
         float a = 0.f;
-        if constexpr (KV == KV_I8) {
+        if constexpr (Scaled<KV>::value) {
 #pragma unroll
           for (int j = 0; j < 2 * NDW; ++j) a = dot2_f16(qv[k][j], kh[j], a);
         } else if constexpr (KV == KV_F32) {
@@ -310,6 +317,8 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
       const bool live = (4 * i + row) < tok_lim;
       if constexpr (KV == KV_I8) {
         sc[i] = live ? (r[0] + q_bias) * (as_f32(ks[i]) * p.scale_log2) : -__builtin_inff();
+      } else if constexpr (KV == KV_E4M3) {
+        sc[i] = live ? r[0] * (as_f32(ks[i]) * p.scale_log2) : -__builtin_inff();
       } else {
         sc[i] = live ? r[0] * p.scale_log2 : -__builtin_inff();
       }
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
 #pragma unroll
     for (int i = 0; i < NL; ++i) pr[i] = (4 * i + row) < tok_lim ? fast_exp2(sc[i] - m_own) : 0.f;
     // tail or skipped block: unwritten slots may hold anything (NaN); INT8 codes are always
-    // finite, and there the scale is masked instead (below)
+    // finite, and there the scale is masked instead (below); E4M3 codes can be NaN
     if (KV != KV_I8 && tok_lim < 16) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
@@ -360,6 +369,28 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
           vp[4 * j + 1] = i8_biased_cross_pair<1>(vd[i][j], vd[i + 1][j]);
           vp[4 * j + 2] = i8_biased_cross_pair<2>(vd[i][j], vd[i + 1][j]);
           vp[4 * j + 3] = i8_biased_cross_pair<3>(vd[i][j], vd[i + 1][j]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const uint32_t ph = bcast_head_u32<G>(pp, h);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = dot2_f16(ph, vp[e], acc[h][e]);
+        }
+      }
+    } else if constexpr (KV == KV_E4M3) {
+#pragma unroll
+      for (int i = 0; i < NL; i += 2) {
+        const float w0 = (4 * i + row) < tok_lim ? pr[i] * as_f32(vs[i]) : 0.f;
+        const float w1 = (4 * i + 4 + row) < tok_lim ? pr[i + 1] * as_f32(vs[i + 1]) : 0.f;
+        l_own += pr[i] + pr[i + 1];
+        const uint32_t pp = pack_f16x2_rne(w0, w1);
+        uint32_t vp[EPL];
+#pragma unroll
+        for (int j = 0; j < NDW; ++j) {
+          vp[4 * j + 0] = e4m3_cross_pair<0>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 1] = e4m3_cross_pair<1>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 2] = e4m3_cross_pair<2>(vd[i][j], vd[i + 1][j]);
+          vp[4 * j + 3] = e4m3_cross_pair<3>(vd[i][j], vd[i + 1][j]);
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -699,11 +730,13 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head
     if (kv_kind == KV_BF16) return launch_parts_kv_d<KV_BF16, 128>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_E5M2) return launch_parts_kv_d<KV_E5M2, 128>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_I8) return launch_parts_kv_d<KV_I8, 128>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_E4M3) return launch_parts_kv_d<KV_E4M3, 128>(p, gqa, num_seqs, stream);
   } else if (head_dim == 64) {
     if (kv_kind == KV_F32) return launch_parts_kv_d<KV_F32, 64>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_BF16) return launch_parts_kv_d<KV_BF16, 64>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_E5M2) return launch_parts_kv_d<KV_E5M2, 64>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_I8) return launch_parts_kv_d<KV_I8, 64>(p, gqa, num_seqs, stream);
+    if (kv_kind == KV_E4M3) return launch_parts_kv_d<KV_E4M3, 64>(p, gqa, num_seqs, stream);
   }
   return hipErrorInvalidValue;
 }

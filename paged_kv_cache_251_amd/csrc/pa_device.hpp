@@ -18,12 +18,18 @@ template <>
 struct KvBytes<KV_E5M2> { static constexpr int value = 1; };
 template <>
 struct KvBytes<KV_I8> { static constexpr int value = 1; };
+template <>
+struct KvBytes<KV_E4M3> { static constexpr int value = 1; };
+
+// Pools whose tiles carry one float32 scale per token after the codes.
+template <int KV>
+struct Scaled { static constexpr bool value = KV == KV_I8 || KV == KV_E4M3; };
 
 // Bytes from the start of one (block, KV head) tile of 16 x D elements to the next: the tile,
-// and for int8 the 16 float32 scales that follow it.
+// and for the scaled kinds the 16 float32 scales that follow it.
 template <int KV, int D>
 struct TileStride {
-  static constexpr int value = 16 * D * KvBytes<KV>::value + (KV == KV_I8 ? 64 : 0);
+  static constexpr int value = 16 * D * KvBytes<KV>::value + (Scaled<KV>::value ? 64 : 0);
 };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -206,6 +212,35 @@ template <int J>
 __device__ __forceinline__ uint32_t i8_biased_cross_pair(uint32_t a, uint32_t b) {
   constexpr uint32_t sel = (uint32_t)J | (0x0Cu << 8) | ((uint32_t)(4 + J) << 16) | (0x0Cu << 24);
   return __builtin_amdgcn_perm(b, a, sel) ^ 0x64806480u;
+}
+
+// FP8 E4M3 (OCP) codes -> f16x2, exact (every E4M3 value is an f16 value), by the matrix-core
+// conversion unit: bytes 0, 1 (HI = false) or 2, 3 (HI = true) of w, low half from the lower byte.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+// (byte j of a, byte j of b) as an f16x2 word, low half from a
+template <int J>
+__device__ __forceinline__ uint32_t e4m3_cross_pair(uint32_t a, uint32_t b) {
+  constexpr uint32_t sel = (uint32_t)J | ((uint32_t)(4 + J) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
+  return e4m3_pair<false>(__builtin_amdgcn_perm(b, a, sel));
+}
+
+// binary32 -> E4M3 code, round to nearest even, saturating at 448; NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_e4m3_sat(float y) {
+  const uint32_t u = as_u32(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;  // |y| >= 448
+  if (a < 0x3C800000u)                        // |y| < 2^-6: steps of 2^-9 (8 steps = 2^-6)
+    return sign | (uint32_t)rintf(as_f32(a) * 512.0f);
+  const uint32_t x = a - (120u << 23);  // exponent bias 127 -> 7
+  uint32_t q = x >> 20;
+  const uint32_t r = x & 0xFFFFFu;
+  q += (r > 0x80000u) | ((r == 0x80000u) & (q & 1u));
+  return sign | (q > 0x7Eu ? 0x7Eu : q);
 }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {

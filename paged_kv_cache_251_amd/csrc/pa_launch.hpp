@@ -7,8 +7,9 @@
 namespace pa {
 
 // Element type of a pool (values match pa_dtype_t).
-// KV_I8: int8 codes with one float32 scale per (token, KV head) after each (block, head) tile
-enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_E5M2 = 2, KV_I8 = 3 };
+// KV_I8, KV_E4M3: 8-bit codes with one float32 scale per (token, KV head) after each (block,
+// head) tile ("scaled" kinds)
+enum KvKind : int { KV_F32 = 0, KV_BF16 = 1, KV_E5M2 = 2, KV_I8 = 3, KV_E4M3 = 4 };
 
 struct DecodeParams {
   void* out;

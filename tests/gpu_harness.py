@@ -14,6 +14,8 @@ import paged_kv_cache_251_amd as pa
 from workloads import POISON_BITS, queries, write_plan
 
 DEV = "cuda:0"
+SCALED = {"int8": torch.int8, "e4m3": torch.float8_e4m3fn}  # scaled pools: torch type of their bytes
+QUANT = {"int8": (oracle.quantize_int8, oracle.dequantize_int8), "e4m3": (oracle.quantize_e4m3, oracle.dequantize_e4m3)}
 TORCH_STORAGE = {"f32": torch.float32, "bf16": torch.bfloat16, "e5m2": torch.uint8}
 INT_VIEW = {"f32": torch.int32, "bf16": torch.int16, "e5m2": torch.uint8}
 
@@ -41,44 +43,46 @@ def to_raw(t: torch.Tensor, dtype: str) -> np.ndarray:
 def poisoned_pool(w, dtype: str | None = None) -> torch.Tensor:
     dtype = dtype or w.kv_dtype
     bits = POISON_BITS[dtype]
-    if dtype == "int8":  # codes then 16 float32 scales per (block, head) tile; every word NaN
+    if dtype in SCALED:  # codes then 16 float32 scales per (block, head) tile; every word NaN
         words = (w.num_blocks, w.num_kv_heads, (w.block_size * w.head_dim + 64) // 4)
-        return torch.full(words, bits, dtype=torch.int32, device=DEV).view(torch.int8)
+        return torch.full(words, bits, dtype=torch.int32, device=DEV).view(SCALED[dtype])
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
     t = torch.full(shape, bits, dtype=INT_VIEW[dtype], device=DEV)
     return t if dtype == "e5m2" else t.view(TORCH_STORAGE[dtype])
 
 
 def int8_canonical(pool: torch.Tensor):
-    """INT8 pool -> (codes [nb, B, Hkv, D] int8, scales [nb, B, Hkv] float32), both in the
-    oracle's layout and token order."""
+    """Scaled pool -> (codes [nb, B, Hkv, D] as raw bytes (uint8), scales [nb, B, Hkv] float32),
+    both in the oracle's layout and token order."""
     codes, scales = pa.int8_pool_split(pool)
-    c = codes.cpu().numpy().transpose(0, 2, 1, 3)
+    c = codes.view(torch.uint8).cpu().numpy().transpose(0, 2, 1, 3)
     slot_of_token = np.argsort(pa.int8_scale_order())  # stored slot -> token order
     sc = scales.cpu().numpy()[:, :, slot_of_token]
     return np.ascontiguousarray(c), np.ascontiguousarray(sc.transpose(0, 2, 1))
 
 
 def oracle_int8_pools(w, phases=("all",), seqs=None):
-    """Oracle INT8 state of a workload: codes, scales (as int8_canonical gives them, NaN scales
-    where nothing was written) and the dequantised float64 pools for the attention oracle."""
+    """Oracle state of a scaled (int8 / e4m3) workload: codes (raw bytes), scales (as
+    int8_canonical gives them, NaN scales where nothing was written) and the dequantised float64
+    pools for the attention oracle."""
+    quant, dequant = QUANT[w.kv_dtype]
     shape = (w.num_blocks, w.block_size, w.num_kv_heads)
     out = {}
     for name in ("k", "v"):
-        codes = np.zeros(shape + (w.head_dim,), np.int8)
+        codes = np.zeros(shape + (w.head_dim,), np.uint8)
         codes_set = np.zeros(shape, bool)
         scales = np.full(shape, np.nan, np.float32)
         for ph in phases:
             plan = write_plan(w, ph, seqs)
             slots = oracle.slot_mapping(w.block_tables, plan.counts, plan.end_pos, w.block_size)
             rows = oracle.decode_storage(getattr(plan, name), w.src_dtype).astype(np.float32)
-            c, sc = oracle.quantize_int8(rows)
+            c, sc = quant(rows)
             keep = slots >= 0
             blk, off = slots[keep] // w.block_size, slots[keep] % w.block_size
-            codes[blk, off] = c[keep]
+            codes[blk, off] = c[keep].view(np.uint8)
             scales[blk, off] = sc[keep]
             codes_set[blk, off] = True
-        deq = oracle.dequantize_int8(codes, scales)
+        deq = dequant(codes.view(np.int8) if w.kv_dtype == "int8" else codes, scales)
         out[name] = (codes, scales, codes_set, deq)
     return out
 

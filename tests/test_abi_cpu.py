@@ -46,7 +46,7 @@ def test_binding_signatures_cover_the_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 3
+    assert lib.pa_abi_version() == 4
     assert lib.pa_status_string(5) == b"out of blocks"
     assert lib.pa_status_string(0) == b"ok"
     assert lib.pa_status_string(3) == b"workspace too small"
@@ -73,6 +73,7 @@ def _decode(lib, **kw):
     (dict(part=16, maxl=64, ws=FAKE, wsb=16), 3), (dict(part=16, maxl=64, ws=FAKE + 64, wsb=1 << 20), 1),
     (dict(nb=1 << 28), 2), (dict(n=70000), 2),
     (dict(qd=0, kd=3), 2), (dict(qd=3, kd=3), 2), (dict(qd=2, kd=3), 2),  # INT8 pools take bf16 queries
+    (dict(qd=0, kd=4), 2), (dict(qd=4, kd=4), 2), (dict(qd=1, kd=5), 1),  # so do FP8_E4M3 pools; 5 is unknown
 ])
 def test_decode_rejects_bad_arguments_on_host(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -100,7 +101,11 @@ def test_cache_write_rejects_bad_arguments_on_host(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 0, 3, None) == 2
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 32, 8, 1, 3, None) == 2
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 96, 16, 8, 1, 3, None) == 2
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 1, 4, None) == 1  # unknown dtype
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 1, 5, None) == 1  # unknown dtype
+    # FP8_E4M3 (scaled) pools: the same limits
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 16, 8, 0, 4, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 128, 32, 8, 1, 4, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 96, 16, 8, 1, 4, None) == 2
 
 
 def test_int8_pool_is_rejected_where_unsupported(lib):
@@ -113,6 +118,11 @@ def test_int8_pool_is_rejected_where_unsupported(lib):
     assert var == 2
     cp = lib.paged_kv_copy_blocks(FAKE, FAKE, FAKE, 1, 2, 128, 32, 8, 3, None)
     assert cp == 2
+    for kd in (3, 4):  # INT8, FP8_E4M3
+        app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16,
+                                                8, 64, 0.1, 1, kd, 0, 0, None, 0, None)
+        assert app == 2
+        assert lib.paged_kv_copy_blocks(FAKE, FAKE, FAKE, 1, 2, 128, 32, 8, kd, None) == 2
 
 
 def test_slot_mapping_rejects_bad_arguments_on_host(lib):

@@ -1,11 +1,12 @@
-"""INT8 KV cache on the GPU against the float64 oracle (needs an MI355X).
+"""Scaled 8-bit KV caches (INT8 and FP8 E4M3 codes with a float32 scale per row) on the GPU
+against the float64 oracle (needs an MI355X).
 
-Bars: the cache write's codes and scales bit-exact against oracle.quantize_int8 on the same
-bf16 rows (a NaN scale where the oracle's is NaN), slots it must not touch left as they were;
-block copies bit-exact; decode attention within the bf16 bar of the oracle run on the
-dequantised pool (code times scale in float64) at edge lengths, every GQA group size, both
-head dims, whole and split contexts, and on sampled sequences of the Llama-3-8B INT8 decode
-batch at full size.
+Bars: the cache write's codes and scales bit-exact against oracle.quantize_int8 /
+oracle.quantize_e4m3 on the same bf16 rows (a NaN scale where the oracle's is NaN), slots it
+must not touch left as they were; block copies bit-exact; decode attention within the bf16 bar
+of the oracle run on the dequantised pool (code value times scale in float64) at edge lengths,
+every GQA group size, both head dims, whole and split contexts, and on sampled sequences of the
+Llama-3-8B decode batch over each pool type at full size.
 """
 import zlib
 
@@ -15,8 +16,8 @@ import torch
 
 import oracle
 import paged_kv_cache_251_amd as pa
-from gpu_harness import (DEV, DeviceBatch, assert_close, int8_canonical, oracle_int8_pools, out_f64,
-                         poisoned_pool, to_device)
+from gpu_harness import (DEV, QUANT, SCALED, DeviceBatch, assert_close, int8_canonical, oracle_int8_pools,
+                         out_f64, poisoned_pool, to_device)
 from workloads import make_config, make_workload, queries
 
 pytestmark = pytest.mark.gpu
@@ -47,8 +48,17 @@ def _special_rows(D, rng):
     return np.stack(rows)
 
 
+KINDS = ["int8", "e4m3"]
+WORKLOAD = {"int8": 7, "e4m3": 8}
+
+
+def _raw_codes(c):
+    return np.asarray(c).view(np.uint8)
+
+
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("D,hkv", [(128, 3), (64, 2)])
-def test_int8_cache_write_bit_exact(D, hkv):
+def test_scaled_cache_write_bit_exact(kind, D, hkv):
     rng = np.random.default_rng(zlib.crc32(f"i8w{D}".encode()))
     special = _special_rows(D, rng)
     n_rand = 300
@@ -61,7 +71,7 @@ def test_int8_cache_write_bit_exact(D, hkv):
     idx = (np.arange(T)[:, None] + 7 * np.arange(hkv)[None, :]) % T
     k, v = rows_k[idx], rows_v[idx]
     nb = (T + 15) // 16 + 3
-    w = make_workload([16], num_q_heads=hkv, num_kv_heads=hkv, head_dim=D, q_dtype="bf16", kv_dtype="int8",
+    w = make_workload([16], num_q_heads=hkv, num_kv_heads=hkv, head_dim=D, q_dtype="bf16", kv_dtype=kind,
                       pool=nb)
     pk, pv = poisoned_pool(w), poisoned_pool(w)
     before = pk.clone()
@@ -71,7 +81,8 @@ def test_int8_cache_write_bit_exact(D, hkv):
     torch.cuda.synchronize()
     for name, src, pool in (("k", k, pk), ("v", v, pv)):
         codes, scales = int8_canonical(pool)
-        want_c, want_s = oracle.quantize_int8(oracle.decode_storage(src, "bf16").astype(np.float32))
+        want_c, want_s = QUANT[kind][0](oracle.decode_storage(src, "bf16").astype(np.float32))
+        want_c = _raw_codes(want_c)
         keep = slots >= 0
         keep &= slots < nb * 16
         blk, off = slots[keep] // 16, slots[keep] % 16
@@ -89,7 +100,8 @@ def test_int8_cache_write_bit_exact(D, hkv):
         assert np.all(np.isnan(scales[~written])), name
 
 
-def test_int8_copy_blocks_bit_exact():
+@pytest.mark.parametrize("kind", KINDS)
+def test_scaled_copy_blocks_bit_exact(kind):
     rng = np.random.default_rng(5)
     nb, hkv, D = 24, 2, 128
     kc = torch.from_numpy(rng.integers(-128, 128, size=(nb, hkv, 16 * D + 64), dtype=np.int8)).to(DEV)
@@ -99,7 +111,7 @@ def test_int8_copy_blocks_bit_exact():
     for s, d in pairs:
         if 0 <= s < nb and 0 <= d < nb and s != d:
             kx[d], vx[d] = kx[s], vx[s]
-    pa.copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV))
+    pa.copy_blocks(kc.view(SCALED[kind]), vc.view(SCALED[kind]), torch.from_numpy(pairs).to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(kc.cpu(), kx) and torch.equal(vc.cpu(), vx)
 
@@ -116,12 +128,13 @@ def _check_pools_match(b, w, o, seqs=None):
         assert np.array_equal(scales[oset].view(np.uint32), os_[oset].view(np.uint32)), name
 
 
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("D,hkv,G", [
     (128, 2, 1), (128, 2, 2), (128, 1, 4), (128, 1, 8), (128, 1, 16), (64, 2, 4), (64, 1, 8), (64, 1, 16),
 ])
-def test_int8_decode_edge_lengths_gqa_and_head_dims(D, hkv, G):
+def test_scaled_decode_edge_lengths_gqa_and_head_dims(kind, D, hkv, G):
     w = make_workload(EDGE_LENS, num_q_heads=hkv * G, num_kv_heads=hkv, head_dim=D, q_dtype="bf16",
-                      src_dtype="bf16", kv_dtype="int8", seed=zlib.crc32(f"i8{D}{hkv}{G}".encode()) % 1000)
+                      src_dtype="bf16", kv_dtype=kind, seed=zlib.crc32(f"i8{D}{hkv}{G}".encode()) % 1000)
     b = DeviceBatch(w)
     o = oracle_int8_pools(w)
     _check_pools_match(b, w, o)
@@ -129,16 +142,17 @@ def test_int8_decode_edge_lengths_gqa_and_head_dims(D, hkv, G):
                               16, w.scale)
     for part in (0, 256, 512, -1):
         got = out_f64(b.decode(part), "bf16")
-        err = assert_close(got, ref, "bf16", f"int8 D{D} G{G} partition {part}")
+        err = assert_close(got, ref, "bf16", f"{kind} D{D} G{G} partition {part}")
         assert np.all(got[0] == 0.0)  # empty context
-    print(f"int8 D{D} G{G}: max abs err {err:.2e}")
+    print(f"{kind} D{D} G{G}: max abs err {err:.2e}")
 
 
-def test_int8_decode_large_values():
-    """Rows with large magnitudes (value scales near 2^7, probabilities up to 2^8 before the lazy
-    max moves): the f16 product of probability and value scale stays in range."""
+@pytest.mark.parametrize("kind", KINDS)
+def test_scaled_decode_large_values(kind):
+    """Rows with large magnitudes (value scales up to ~2^7, probabilities up to 2^8 before the
+    lazy max moves): the f16 product of probability and value scale stays in range."""
     w = make_workload([700, 33], num_q_heads=8, num_kv_heads=2, head_dim=128, q_dtype="bf16", src_dtype="bf16",
-                      kv_dtype="int8", seed=77)
+                      kv_dtype=kind, seed=77)
     b = DeviceBatch(w, phases=())
     from workloads import write_plan
 
@@ -149,9 +163,10 @@ def test_int8_decode_large_values():
     end = torch.from_numpy(plan.end_pos).to(DEV)
     slots = pa.slot_mapping(cu, end, b.tables, plan.num_tokens, w.num_blocks, 16)
     pa.kv_cache_write(to_device(big_k, "bf16"), to_device(big_v, "bf16"), b.pk, b.pv, slots)
-    ck, sk = oracle.quantize_int8(oracle.decode_storage(big_k, "bf16").astype(np.float32))
-    cv, sv = oracle.quantize_int8(oracle.decode_storage(big_v, "bf16").astype(np.float32))
-    kd, vd = oracle.dequantize_int8(ck, sk), oracle.dequantize_int8(cv, sv)
+    quant, dequant = QUANT[kind]
+    ck, sk = quant(oracle.decode_storage(big_k, "bf16").astype(np.float32))
+    cv, sv = quant(oracle.decode_storage(big_v, "bf16").astype(np.float32))
+    kd, vd = dequant(ck, sk), dequant(cv, sv)
     q = oracle.decode_storage(queries(w), "bf16")
     ref, start = [], 0
     for s in range(w.num_seqs):
@@ -175,8 +190,9 @@ def _sample(w, k, seed):
     return sorted(pick)
 
 
-def test_int8_decode_full_size_sampled():
-    w = make_config(7)
+@pytest.mark.parametrize("kind", KINDS)
+def test_scaled_decode_full_size_sampled(kind):
+    w = make_config(WORKLOAD[kind])
     b = DeviceBatch(w)
     sel = _sample(w, 6, 41)
     o = oracle_int8_pools(w, seqs=sel)
@@ -185,5 +201,5 @@ def test_int8_decode_full_size_sampled():
                               w.scale, seqs=sel)
     for part in (-1, 512):
         out = out_f64(b.decode(part), "bf16")[sel]
-        err = assert_close(out, ref, "bf16", f"int8 full size partition {part}")
-        print(f"int8 full size partition {part}: max abs err {err:.2e}")
+        err = assert_close(out, ref, "bf16", f"{kind} full size partition {part}")
+        print(f"{kind} full size partition {part}: max abs err {err:.2e}")

@@ -7,6 +7,7 @@ Storage conventions (raw bits, as they sit in device memory):
             code under test, never here)
   'int8' -> int8 codes with a float32 scale per (token, KV head) row (a cache dtype
             only, like 'e5m2')
+  'e4m3' -> FP8 E4M3 codes with a float32 scale per row (a cache dtype only)
 
 Every random draw comes from ``np.random.default_rng([seed, stream, ...])`` so
 that one sequence's keys and values can be regenerated on their own, which
@@ -22,15 +23,15 @@ from dataclasses import dataclass
 import numpy as np
 
 STORAGE = {"f32": np.float32, "bf16": np.uint16, "e5m2": np.uint8}
-ITEMSIZE = {"f32": 4, "bf16": 2, "e5m2": 1, "int8": 1}
+ITEMSIZE = {"f32": 4, "bf16": 2, "e5m2": 1, "int8": 1, "e4m3": 1}
 # bytes a pool stores per (token, KV head) row besides its head_dim elements
-ROW_EXTRA = {"f32": 0, "bf16": 0, "e5m2": 0, "int8": 4}
+ROW_EXTRA = {"f32": 0, "bf16": 0, "e5m2": 0, "int8": 4, "e4m3": 4}
 
 # Quiet-NaN patterns written over a pool before any cache write: a read of a
 # slot that was never written (the tail of a last block, a spare block) then
 # turns the output into NaN instead of going unnoticed.
 POISON_BITS = {"f32": 0x7FC00000, "bf16": 0x7FC0, "e5m2": 0x7F,
-               "int8": 0x7FC00000}  # int8: every 32-bit word, so every scale is NaN
+               "int8": 0x7FC00000, "e4m3": 0x7FC00000}  # scaled pools: every 32-bit word, so every scale is NaN
 
 CONFIG_NAMES = {
     1: "tiny_decode_fp32",
@@ -40,6 +41,7 @@ CONFIG_NAMES = {
     5: "varlen_prefill_decode_bf16",
     6: "llama3_8b_spec_verify_k4_bf16",
     7: "llama3_8b_decode_int8_kv",
+    8: "llama3_8b_decode_fp8_e4m3_scaled_kv",
 }
 
 # random streams
@@ -276,6 +278,11 @@ def make_config(idx: int, replica: int = 0) -> Workload:
         lens = rl.integers(256, 4096 + 1, size=128)
         return make_workload(lens, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
                              src_dtype="bf16", kv_dtype="int8", seed=seed, name=name)
+    if idx == 8:
+        # the same batch over a scaled FP8 E4M3 pool
+        lens = rl.integers(256, 4096 + 1, size=128)
+        return make_workload(lens, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
+                             src_dtype="bf16", kv_dtype="e4m3", seed=seed, name=name)
     raise ValueError(f"no workload {idx}")
 
 
