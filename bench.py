@@ -520,31 +520,42 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the kernel sources: measured traffic only counts for the sources it was
-    measured on."""
+# Sources each measured kernel is built and launched from: its traffic figure only counts while
+# they are unchanged.
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
+    "multiquery": ("multiquery.hip", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
+}
+
+
+def kernel_family(workload: str) -> str:
+    return "multiquery" if workload.startswith("llama3_8b_spec_verify") else "decode"
+
+
+def kernel_source_digest(family: str) -> str:
+    """sha256 over the sources of one kernel family: measured traffic only counts for the
+    sources it was measured on."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "paged_kv_cache_251_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in KERNEL_SOURCES[family]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
 def measured_traffic(path, workload):
-    """HBM bytes per launch of the partition kernel for this workload, from the committed
+    """HBM bytes per launch of the dominant kernel for this workload, from the committed
     rocprofv3 counter summary, or None when it is missing or was taken on other sources."""
     if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
-        return None
     entry = rec.get("workloads", {}).get(workload)
-    return None if entry is None else entry.get("hbm_bytes_per_launch")
+    if entry is None or entry.get("source_sha256") != kernel_source_digest(kernel_family(workload)):
+        return None
+    return entry.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(w, budget_s):
