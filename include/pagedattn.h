@@ -76,7 +76,8 @@
  *     inputs are unspecified but no access leaves the buffers described here.
  *   - Supported now: block_size 16; head_dim 64 or 128; gqa_group 1, 2, 4, 8 or 16;
  *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), and (BF16, INT8) and
- *     (BF16, FP8_E4M3) for the decode calls without append.
+ *     (BF16, FP8_E4M3) for the decode calls without append; packed (varlen) batches take
+ *     (BF16, BF16) and (BF16, FP8_E5M2).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -300,8 +301,9 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
  * serves all its rows, otherwise 128-row query tiles.  When total_q = num_seqs * max_q_len and
  * max_q_len >= 2 no sequence has a single row and the decode kernel is not launched; when
  * max_q_len <= 1 only the decode kernel is.
- * Supported: bf16 query and cache.  A row whose position is negative (n_s > L) sees no key and
- * comes out zero.
+ * Supported: bf16 query; bf16 or FP8_E5M2 cache (E5M2 codes widen exactly to f16, and the
+ * multi-token rows then run on the f16 MFMA with the query and the probabilities in f16).  A row
+ * whose position is negative (n_s > L) sees no key and comes out zero.
  */
 pa_status_t paged_attention_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,
                                    const int32_t* cu_seqlens_q, const int32_t* context_lens,

@@ -419,8 +419,8 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
                                   max_context_len, scale, q_dtype, kv_dtype, partition_size, workspace,
                                   workspace_bytes, true);
   if (st != PA_OK) return st;
-  if (q_dtype != PA_BF16 || kv_dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "%s: packed batches take bf16 queries and a bf16 cache", fn);
+  if (q_dtype != PA_BF16 || (kv_dtype != PA_BF16 && kv_dtype != PA_FP8_E5M2))
+    return fail(PA_ERR_UNSUPPORTED, "%s: packed batches take bf16 queries and a bf16 or FP8_E5M2 cache", fn);
   if (num_seqs == 0 || total_q == 0) return ok();
   if (!cu_seqlens_q || !aligned(cu_seqlens_q, 4)) return fail(PA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens_q", fn);
   const int64_t prefill_tiles = (static_cast<int64_t>(max_q_len) * gqa_group + 127) / 128;
@@ -437,9 +437,9 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
   }
   if (e == hipSuccess && max_q_len >= 2) {  // some sequence may have several rows
     if (pa::multiquery_applies(gqa_group, max_q_len))
-      e = pa::launch_varlen_multiquery(p, head_dim, gqa_group, num_seqs, max_q_len, stream);
+      e = pa::launch_varlen_multiquery(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, max_q_len, stream);
     else
-      e = pa::launch_varlen_prefill(p, head_dim, gqa_group, num_seqs, total_q, max_q_len, stream);
+      e = pa::launch_varlen_prefill(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, total_q, max_q_len, stream);
   }
   return device_status(e, fn);
 }

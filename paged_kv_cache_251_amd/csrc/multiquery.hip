@@ -20,6 +20,7 @@
 //                                          ds_read_b64_tr_b16
 // Row sums come from the same rounded weights through an MFMA with a ones matrix.
 #include <atomic>
+#include <type_traits>
 
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
@@ -35,13 +36,27 @@ typedef short mq_v4i16_t __attribute__((ext_vector_type(4)));
 constexpr float kTauMq = 8.0f;
 constexpr int kMaxRankedMq = 1024;
 
+typedef __attribute__((ext_vector_type(8))) _Float16 mq_f16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 mq_f16x4_t;
+
+// bf16 MFMAs, or f16 ones for an E5M2 cache (E8)
+template <bool E8>
 __device__ __forceinline__ mq_f32x4_t mfma_k32(const uint4& a, const uint4& b, const mq_f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8_t, a), __builtin_bit_cast(mq_bf16x8_t, b),
-                                                 c, 0, 0, 0);
+  if constexpr (E8)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mq_f16x8_t, a), __builtin_bit_cast(mq_f16x8_t, b),
+                                                  c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mq_bf16x8_t, a),
+                                                   __builtin_bit_cast(mq_bf16x8_t, b), c, 0, 0, 0);
 }
+template <bool E8>
 __device__ __forceinline__ mq_f32x4_t mfma_k16(const uint2& a, const uint2& b, const mq_f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mq_v4i16_t, a), __builtin_bit_cast(mq_v4i16_t, b),
-                                                   c, 0, 0, 0);
+  if constexpr (E8)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(mq_f16x4_t, a), __builtin_bit_cast(mq_f16x4_t, b),
+                                                 c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(mq_v4i16_t, a),
+                                                     __builtin_bit_cast(mq_v4i16_t, b), c, 0, 0, 0);
 }
 // ds_read_b64_tr_b16: within each 16-lane group, lane i's j-th 16-bit result is element i % 4 of
 // the 8 bytes read by lane 4 j + i / 4 (checked on the device)
@@ -52,7 +67,9 @@ __device__ __forceinline__ uint2 mq_read_tr16(const uint16_t* p) {
 
 }  // namespace
 
-template <int D, int G, int NT>
+// E8: the cache holds E5M2 codes, widened to f16 as they are loaded; queries and probabilities
+// in f16 and the products on the f16 MFMA.
+template <int D, int G, int NT, bool E8>
 __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeParams p) {
   constexpr int W = 4;
   constexpr int ROWS = NT * 16;       // query rows of the work-group: row r = (token r / G, head r % G)
@@ -101,7 +118,10 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
         reinterpret_cast<const uint16_t*>(p.query) + ((size_t)(a + (ok ? tok[j] : 0)) * hq + (size_t)g * G + r % G) * D;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg);
+      uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg);
+      if constexpr (E8)
+        v = make_uint4(pack_f16x2_rne(bf16lo(v.x), bf16hi(v.x)), pack_f16x2_rne(bf16lo(v.y), bf16hi(v.y)),
+                       pack_f16x2_rne(bf16lo(v.z), bf16hi(v.z)), pack_f16x2_rne(bf16lo(v.w), bf16hi(v.w)));
       qb[j][kk] = ok ? v : make_uint4(0, 0, 0, 0);
     }
   }
@@ -119,19 +139,21 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) oacc[j][dt] = mq_f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const uint2 kOnes = make_uint2(0x3F803F80u, 0x3F803F80u);  // bf16 1.0 x4
+  constexpr uint32_t ONE2 = E8 ? 0x3C003C00u : 0x3F803F80u;  // (f16 or bf16) 1.0 x2
+  const uint2 kOnes = make_uint2(ONE2, ONE2);
+  constexpr int SZ = E8 ? 1 : 2;  // cache bytes per element
 
   const int* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
   const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.key_cache);
   const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.value_cache);
-  const size_t blk_bytes = (size_t)p.num_kv_heads * 16 * D * 2;
-  const uint32_t k_off = (uint32_t)(((g * 16 + lr) * D + 8 * lg) * 2);  // + 64 kk bytes
+  const size_t blk_bytes = (size_t)p.num_kv_heads * 16 * D * SZ;
+  const uint32_t k_off = (uint32_t)(((g * 16 + lr) * D + 8 * lg) * SZ);  // + 32 kk elements
   uint32_t v_off[VLD];
   int v_lds[VLD];
 #pragma unroll
   for (int u = 0; u < VLD; ++u) {
     const int q = lane + 64 * u, key = q / CH, c = q % CH;
-    v_off[u] = (uint32_t)(((g * 16 + key) * D + c * 8) * 2);
+    v_off[u] = (uint32_t)(((g * 16 + key) * D + c * 8) * SZ);
     v_lds[u] = key * VP + c * 8;
   }
   uint16_t* vs = reinterpret_cast<uint16_t*>(lds) + wave * VWAVE;
@@ -149,12 +171,17 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
     phys = t.ok ? phys : 0;
     const uint8_t* kb = kc + (size_t)phys * blk_bytes;
     const uint8_t* vb = vc + (size_t)phys * blk_bytes;
-    auto ld16 = [](const uint8_t* q) {
-      const u32x4_t v = ld<u32x4_t, true>(q);  // streamed once
-      return make_uint4(v.x, v.y, v.z, v.w);
+    auto ld16 = [](const uint8_t* q) {  // 8 elements as bf16 (or f16 widened from E5M2)
+      if constexpr (E8) {
+        const u32x2_t v = ld<u32x2_t, true>(q);  // streamed once
+        return make_uint4(e5m2_pair_lo(v.x), e5m2_pair_hi(v.x), e5m2_pair_lo(v.y), e5m2_pair_hi(v.y));
+      } else {
+        const u32x4_t v = ld<u32x4_t, true>(q);  // streamed once
+        return make_uint4(v.x, v.y, v.z, v.w);
+      }
     };
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) t.k[kk] = ld16(kb + k_off + 64 * kk);
+    for (int kk = 0; kk < KS; ++kk) t.k[kk] = ld16(kb + k_off + 32 * kk * SZ);
 #pragma unroll
     for (int u = 0; u < VLD; ++u) t.v[u] = ld16(vb + v_off[u]);
     __builtin_amdgcn_sched_barrier(0);  // issue the block before the math that follows
@@ -173,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
     for (int j = 0; j < NT; ++j) {
       mq_f32x4_t sa = mq_f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) sa = mfma_k32(t.k[kk], qb[j][kk], sa);
+      for (int kk = 0; kk < KS; ++kk) sa = mfma_k32<E8>(t.k[kk], qb[j][kk], sa);
       float sv[4];
       float mx = -__builtin_inff();
 #pragma unroll
@@ -196,17 +223,18 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
         m_run[j] = mn;
       }
       const float mneg = m_run[j] == -__builtin_inff() ? 0.f : -m_run[j];
-      __bf16 pb[4];
+      typedef std::conditional_t<E8, _Float16, __bf16> pel_t;
+      pel_t pb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = (__bf16)fast_exp2(fmaf(sv[i], p.scale_log2, mneg));  // -inf -> 0
+      for (int i = 0; i < 4; ++i) pb[i] = (pel_t)fast_exp2(fmaf(sv[i], p.scale_log2, mneg));  // -inf -> 0
       const uint2 pt = make_uint2(
           (uint32_t)__builtin_bit_cast(uint16_t, pb[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, pb[1]) << 16),
           (uint32_t)__builtin_bit_cast(uint16_t, pb[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, pb[3]) << 16));
-      lacc[j] = mfma_k16(kOnes, pt, lacc[j]);
+      lacc[j] = mfma_k16<E8>(kOnes, pt, lacc[j]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const uint2 va = mq_read_tr16(vs + v_rd + dt * 16);  // V^T[dims dt*16 + lr][keys 4lg..]
-        oacc[j][dt] = mfma_k16(va, pt, oacc[j][dt]);
+        oacc[j][dt] = mfma_k16<E8>(va, pt, oacc[j][dt]);
       }
     }
   };
@@ -287,9 +315,9 @@ int mq_device_cus() {
   return cus;
 }
 
-template <int D, int G, int NT>
+template <int D, int G, int NT, bool E8>
 hipError_t launch_mq_dgn(const DecodeParams& p, int num_seqs, hipStream_t stream) {
-  auto kernel = varlen_multiquery_kernel<D, G, NT>;
+  auto kernel = varlen_multiquery_kernel<D, G, NT, E8>;
   DecodeParams q = p;
   q.longest_first = num_seqs <= kMaxRankedMq ? 1 : 0;
   q.snake = 0;
@@ -306,20 +334,20 @@ hipError_t launch_mq_dgn(const DecodeParams& p, int num_seqs, hipStream_t stream
   return hipGetLastError();
 }
 
-template <int D, int G>
+template <int D, int G, bool E8>
 hipError_t launch_mq_dg(const DecodeParams& p, int num_seqs, int max_q_len, hipStream_t stream) {
-  if (max_q_len * G <= 16) return launch_mq_dgn<D, G, 1>(p, num_seqs, stream);
-  return launch_mq_dgn<D, G, 2>(p, num_seqs, stream);
+  if (max_q_len * G <= 16) return launch_mq_dgn<D, G, 1, E8>(p, num_seqs, stream);
+  return launch_mq_dgn<D, G, 2, E8>(p, num_seqs, stream);
 }
 
-template <int D>
+template <int D, bool E8>
 hipError_t launch_mq_d(const DecodeParams& p, int gqa, int num_seqs, int max_q_len, hipStream_t stream) {
   switch (gqa) {
-    case 1: return launch_mq_dg<D, 1>(p, num_seqs, max_q_len, stream);
-    case 2: return launch_mq_dg<D, 2>(p, num_seqs, max_q_len, stream);
-    case 4: return launch_mq_dg<D, 4>(p, num_seqs, max_q_len, stream);
-    case 8: return launch_mq_dg<D, 8>(p, num_seqs, max_q_len, stream);
-    case 16: return launch_mq_dg<D, 16>(p, num_seqs, max_q_len, stream);
+    case 1: return launch_mq_dg<D, 1, E8>(p, num_seqs, max_q_len, stream);
+    case 2: return launch_mq_dg<D, 2, E8>(p, num_seqs, max_q_len, stream);
+    case 4: return launch_mq_dg<D, 4, E8>(p, num_seqs, max_q_len, stream);
+    case 8: return launch_mq_dg<D, 8, E8>(p, num_seqs, max_q_len, stream);
+    case 16: return launch_mq_dg<D, 16, E8>(p, num_seqs, max_q_len, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -328,11 +356,17 @@ hipError_t launch_mq_d(const DecodeParams& p, int gqa, int num_seqs, int max_q_l
 
 bool multiquery_applies(int gqa, int max_q_len) { return max_q_len >= 2 && max_q_len * gqa <= 32; }
 
-hipError_t launch_varlen_multiquery(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
-                                    hipStream_t stream) {
+hipError_t launch_varlen_multiquery(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
+                                    int max_q_len, hipStream_t stream) {
   if (!multiquery_applies(gqa, max_q_len)) return hipErrorInvalidValue;
-  if (head_dim == 128) return launch_mq_d<128>(p, gqa, num_seqs, max_q_len, stream);
-  if (head_dim == 64) return launch_mq_d<64>(p, gqa, num_seqs, max_q_len, stream);
+  const bool e8 = kv_kind == KV_E5M2;
+  if (!e8 && kv_kind != KV_BF16) return hipErrorInvalidValue;
+  if (head_dim == 128)
+    return e8 ? launch_mq_d<128, true>(p, gqa, num_seqs, max_q_len, stream)
+              : launch_mq_d<128, false>(p, gqa, num_seqs, max_q_len, stream);
+  if (head_dim == 64)
+    return e8 ? launch_mq_d<64, true>(p, gqa, num_seqs, max_q_len, stream)
+              : launch_mq_d<64, false>(p, gqa, num_seqs, max_q_len, stream);
   return hipErrorInvalidValue;
 }
 

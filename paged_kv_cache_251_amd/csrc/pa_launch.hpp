@@ -62,11 +62,11 @@ hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_d
 // Multi-token rows of a packed batch when every sequence has at most max_q_len tokens and
 // max_q_len * gqa <= 32 (speculative verification): one work-group streams each context once.
 bool multiquery_applies(int gqa, int max_q_len);
-hipError_t launch_varlen_multiquery(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int max_q_len,
-                                    hipStream_t stream);
+hipError_t launch_varlen_multiquery(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
+                                    int max_q_len, hipStream_t stream);
 
-// Prefill rows (sequences with >= 2 query tokens) of a packed batch, on MFMA.
-hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int total_q,
+// Prefill rows (sequences with >= 2 query tokens) of a packed batch, on MFMA (bf16 or E5M2 cache).
+hipError_t launch_varlen_prefill(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs, int total_q,
                                  int max_q_len, hipStream_t stream);
 
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* cu, const int32_t* end_pos,

@@ -32,6 +32,7 @@
 // longest units first across all chunks, and the grid's spare work-groups come last.
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
@@ -52,12 +53,32 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+
+// 16x16x32 MFMA on bf16 operands, or on f16 operands for an E5M2 cache (E8)
+template <bool E8>
 __device__ __forceinline__ f32x4_t mfma_16x16x32(const uint4& a, const uint4& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
+  if constexpr (E8)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                  0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
 }
 
-template <int D, int G>
+// 8 E5M2 codes -> 8 f16 (exact: a code is the upper byte of the f16 of the same value)
+__device__ __forceinline__ uint4 widen_e5m2x8(uint2 w) {
+  return make_uint4(e5m2_pair_lo(w.x), e5m2_pair_hi(w.x), e5m2_pair_lo(w.y), e5m2_pair_hi(w.y));
+}
+// 8 bf16 -> 8 f16, each rounded to nearest even (exact within f16's range)
+__device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w) {
+  return make_uint4(pack_f16x2_rne(bf16lo(w.x), bf16hi(w.x)), pack_f16x2_rne(bf16lo(w.y), bf16hi(w.y)),
+                    pack_f16x2_rne(bf16lo(w.z), bf16hi(w.z)), pack_f16x2_rne(bf16lo(w.w), bf16hi(w.w)));
+}
+
+// E8: the cache holds E5M2 codes; they are widened to f16 on their way into LDS, the queries
+// are taken to f16 and the products run on the f16 MFMA (probabilities in f16).
+template <int D, int G, bool E8>
 __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodeParams p) {
   constexpr int W = 4, NT = 2;            // waves; 16-row MFMA tiles per wave
   constexpr int ROWS = W * NT * 16;       // query rows per work-group
@@ -214,6 +235,7 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg);
+      if constexpr (E8) v = bf16x8_to_f16(v);
       qb[j][kk] = ok ? v : make_uint4(0, 0, 0, 0);
     }
   }
@@ -234,11 +256,20 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
   const int tok_first = i0 + (wave * NT * 16) / G;
   const int tok_last = i0 + (wave * NT * 16 + NT * 16 - 1) / G;
   const int wave_lim_min = tok_last >= n ? 0 : (causal ? min(L, L - n + tok_first + 1) : L);
-  const uint4 kOnes = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 x8
+  constexpr uint32_t ONE2 = E8 ? 0x3C003C00u : 0x3F803F80u;  // (f16 or bf16) 1.0 x2
+  const uint4 kOnes = make_uint4(ONE2, ONE2, ONE2, ONE2);
 
   const int* table = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-  const uint16_t* kc = reinterpret_cast<const uint16_t*>(p.key_cache);
-  const uint16_t* vc = reinterpret_cast<const uint16_t*>(p.value_cache);
+  constexpr int SZ = E8 ? 1 : 2;  // cache bytes per element
+  const uint8_t* kc = reinterpret_cast<const uint8_t*>(p.key_cache);
+  const uint8_t* vc = reinterpret_cast<const uint8_t*>(p.value_cache);
+  // the 8 elements of a chunk, as 8 bf16 (or f16 widened from E5M2)
+  auto ld_chunk = [](const uint8_t* q) -> uint4 {
+    if constexpr (E8)
+      return widen_e5m2x8(*reinterpret_cast<const uint2*>(q));
+    else
+      return *reinterpret_cast<const uint4*>(q);
+  };
 
   const int ntiles = (kv_end + KT - 1) / KT;
   // Tile kt+1 is fetched into registers while tile kt is multiplied; K and V chunks are taken
@@ -281,10 +312,10 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
         const int phys = block_of(u);
-        const uint16_t* kb = kc + (size_t)phys * blk_stride;
-        const uint16_t* vb = vc + (size_t)phys * blk_stride;
-        kreg[u] = *reinterpret_cast<const uint4*>(kb + lane_off);
-        vreg[u] = *reinterpret_cast<const uint4*>(vb + lane_off);
+        const uint8_t* kb = kc + (size_t)phys * blk_stride * SZ;
+        const uint8_t* vb = vc + (size_t)phys * blk_stride * SZ;
+        kreg[u] = ld_chunk(kb + (size_t)lane_off * SZ);
+        vreg[u] = ld_chunk(vb + (size_t)lane_off * SZ);
       }
       return;
     }
@@ -293,10 +324,10 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
       const int phys = block_of(u);
       const int kidx = kt * KT + (tid + 256 * u) / CH;
       const bool ok = kidx < kv_end && phys >= 0;
-      const uint16_t* kb = kc + (size_t)(ok ? phys : 0) * blk_stride;
-      const uint16_t* vb = vc + (size_t)(ok ? phys : 0) * blk_stride;
-      const uint4 kv4 = *reinterpret_cast<const uint4*>(kb + lane_off);
-      const uint4 vv4 = *reinterpret_cast<const uint4*>(vb + lane_off);
+      const uint8_t* kb = kc + (size_t)(ok ? phys : 0) * blk_stride * SZ;
+      const uint8_t* vb = vc + (size_t)(ok ? phys : 0) * blk_stride * SZ;
+      const uint4 kv4 = ld_chunk(kb + (size_t)lane_off * SZ);
+      const uint4 vv4 = ld_chunk(vb + (size_t)lane_off * SZ);
       kreg[u] = ok ? kv4 : make_uint4(0, 0, 0, 0);  // unwritten slots may hold NaN: zero them
       vreg[u] = ok ? vv4 : make_uint4(0, 0, 0, 0);
     }
@@ -342,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
       for (int m = 0; m < 4; ++m) {
         const uint4 ka = *reinterpret_cast<const uint4*>(Ks + (m * 16 + lr) * KP + 32 * kk + 8 * lg);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) sacc[j][m] = mfma_16x16x32(ka, qb[j][kk], sacc[j][m]);
+        for (int j = 0; j < NT; ++j) sacc[j][m] = mfma_16x16x32<E8>(ka, qb[j][kk], sacc[j][m]);
       }
     }
 
@@ -390,17 +421,18 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
       uint32_t pk[4][2];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        __bf16 b[4];
+        typedef std::conditional_t<E8, _Float16, __bf16> pel_t;
+        pel_t b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = (__bf16)fast_exp2(fmaf(sv[m][i], p.scale_log2, mneg));  // -inf -> 0
+        for (int i = 0; i < 4; ++i) b[i] = (pel_t)fast_exp2(fmaf(sv[m][i], p.scale_log2, mneg));  // -inf -> 0
         pk[m][0] = (uint32_t)__builtin_bit_cast(uint16_t, b[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, b[1]) << 16);
         pk[m][1] = (uint32_t)__builtin_bit_cast(uint16_t, b[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, b[3]) << 16);
       }
       pb[j][0] = make_uint4(pk[0][0], pk[0][1], pk[1][0], pk[1][1]);  // keys 4lg.. , 16+4lg..
       pb[j][1] = make_uint4(pk[2][0], pk[2][1], pk[3][0], pk[3][1]);  // keys 32+4lg.., 48+4lg..
       // row sums of the same rounded weights, on the matrix core: ones . P^T
-      lacc[j] = mfma_16x16x32(kOnes, pb[j][0], lacc[j]);
-      lacc[j] = mfma_16x16x32(kOnes, pb[j][1], lacc[j]);
+      lacc[j] = mfma_16x16x32<E8>(kOnes, pb[j][0], lacc[j]);
+      lacc[j] = mfma_16x16x32<E8>(kOnes, pb[j][1], lacc[j]);
     }
 
     // ---- O^T += V^T P^T --------------------------------------------------------------------
@@ -413,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
         const uint2 l2 = lds_read_tr16(vsrc), h2 = lds_read_tr16(vsrc + 16 * VP);
         const uint4 va = make_uint4(l2.x, l2.y, h2.x, h2.y);  // V[keys sigma][dim dt*16 + lr]
 #pragma unroll
-        for (int j = 0; j < NT; ++j) oacc[j][dt] = mfma_16x16x32(va, pb[j][ks], oacc[j][dt]);
+        for (int j = 0; j < NT; ++j) oacc[j][dt] = mfma_16x16x32<E8>(va, pb[j][ks], oacc[j][dt]);
       }
     }
     if (kt + 1 < ntiles) {
@@ -443,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void varlen_prefill_kernel(const DecodePara
   }
 }
 
-template <int D, int G>
+template <int D, int G, bool E8>
 static hipError_t launch_prefill_dg(const DecodeParams& p, int num_seqs, int total_q, int max_q_len,
                                    hipStream_t stream) {
   constexpr int TOKW = 128 / G;
@@ -455,34 +487,40 @@ static hipError_t launch_prefill_dg(const DecodeParams& p, int num_seqs, int tot
     const long long chunks = std::min<long long>(num_seqs, total_q / 2);
     const long long units = std::min<long long>((total_q + chunks * (TOKW - 1)) / TOKW, tiles_per_seq * num_seqs);
     q.sched_seqs = num_seqs;
-    hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), dim3((unsigned)(units * p.num_kv_heads)), dim3(256), 0,
+    hipLaunchKernelGGL((varlen_prefill_kernel<D, G, E8>), dim3((unsigned)(units * p.num_kv_heads)), dim3(256), 0,
                        stream, q);
   } else {
     q.sched_seqs = 0;
     dim3 grid(p.num_kv_heads, (unsigned)tiles_per_seq, num_seqs);
-    hipLaunchKernelGGL((varlen_prefill_kernel<D, G>), grid, dim3(256), 0, stream, q);
+    hipLaunchKernelGGL((varlen_prefill_kernel<D, G, E8>), grid, dim3(256), 0, stream, q);
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool E8>
 static hipError_t launch_prefill_d(const DecodeParams& p, int gqa, int num_seqs, int total_q, int max_q_len,
                                    hipStream_t stream) {
   switch (gqa) {
-    case 1: return launch_prefill_dg<D, 1>(p, num_seqs, total_q, max_q_len, stream);
-    case 2: return launch_prefill_dg<D, 2>(p, num_seqs, total_q, max_q_len, stream);
-    case 4: return launch_prefill_dg<D, 4>(p, num_seqs, total_q, max_q_len, stream);
-    case 8: return launch_prefill_dg<D, 8>(p, num_seqs, total_q, max_q_len, stream);
-    case 16: return launch_prefill_dg<D, 16>(p, num_seqs, total_q, max_q_len, stream);
+    case 1: return launch_prefill_dg<D, 1, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 2: return launch_prefill_dg<D, 2, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 4: return launch_prefill_dg<D, 4, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 8: return launch_prefill_dg<D, 8, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 16: return launch_prefill_dg<D, 16, E8>(p, num_seqs, total_q, max_q_len, stream);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_varlen_prefill(const DecodeParams& p, int head_dim, int gqa, int num_seqs, int total_q,
+hipError_t launch_varlen_prefill(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs, int total_q,
                                  int max_q_len, hipStream_t stream) {
   if (max_q_len <= 1) return hipSuccess;  // no sequence has two or more query tokens
-  if (head_dim == 128) return launch_prefill_d<128>(p, gqa, num_seqs, total_q, max_q_len, stream);
-  if (head_dim == 64) return launch_prefill_d<64>(p, gqa, num_seqs, total_q, max_q_len, stream);
+  const bool e8 = kv_kind == KV_E5M2;
+  if (!e8 && kv_kind != KV_BF16) return hipErrorInvalidValue;
+  if (head_dim == 128)
+    return e8 ? launch_prefill_d<128, true>(p, gqa, num_seqs, total_q, max_q_len, stream)
+              : launch_prefill_d<128, false>(p, gqa, num_seqs, total_q, max_q_len, stream);
+  if (head_dim == 64)
+    return e8 ? launch_prefill_d<64, true>(p, gqa, num_seqs, total_q, max_q_len, stream)
+              : launch_prefill_d<64, false>(p, gqa, num_seqs, total_q, max_q_len, stream);
   return hipErrorInvalidValue;
 }
 

@@ -113,9 +113,10 @@ def test_int8_pool_is_rejected_where_unsupported(lib):
     app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
                                             64, 0.1, 1, 3, 0, 0, None, 0, None)
     assert app == 2 and b"INT8" in lib.pa_last_error()
-    var = lib.paged_attention_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 2, 2, 2, 128, 16, 8, 64,
-                                     0.1, 1, 1, 3, 0, None, 0, None)
-    assert var == 2
+    for kd in (0, 3, 4):  # packed batches take bf16 or FP8_E5M2 pools only
+        var = lib.paged_attention_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 2, 2, 2, 128, 16, 8, 64,
+                                         0.1, 1, 1, kd, 0, None, 0, None)
+        assert var == 2
     cp = lib.paged_kv_copy_blocks(FAKE, FAKE, FAKE, 1, 2, 128, 32, 8, 3, None)
     assert cp == 2
     for kd in (3, 4):  # INT8, FP8_E4M3

@@ -40,18 +40,20 @@ def test_spec_verify_workload_full_size():
     print(f"spec verify k=4: max abs err {err:.2e}")
 
 
-@pytest.mark.parametrize("k,G,D", [(2, 4, 128), (3, 8, 128), (5, 1, 128), (8, 4, 64), (16, 2, 64), (4, 16, 128)])
-def test_spec_verify_draft_lengths(k, G, D):
+@pytest.mark.parametrize("k,G,D,kv", [(2, 4, 128, "bf16"), (3, 8, 128, "bf16"), (5, 1, 128, "bf16"), (8, 4, 64, "bf16"),
+                                      (16, 2, 64, "bf16"), (4, 16, 128, "bf16"), (4, 4, 128, "e5m2"),
+                                      (3, 8, 128, "e5m2"), (16, 2, 64, "e5m2")])
+def test_spec_verify_draft_lengths(k, G, D, kv):
     rng = np.random.default_rng(zlib.crc32(f"spec{k}{G}{D}".encode()))
     cached = np.array([0, 1, 15, 16, 17, 31, 64, 100, 255, 1000])
     lens = cached + k
     w = make_workload(lens[rng.permutation(len(lens))], q_lens=np.full(len(lens), k), num_q_heads=2 * G,
-                      num_kv_heads=2, head_dim=D, q_dtype="bf16", seed=k * 100 + G)
+                      num_kv_heads=2, head_dim=D, q_dtype="bf16", src_dtype="bf16", kv_dtype=kv, seed=k * 100 + G)
     b = DeviceBatch(w)
     pk, pv = oracle_pools(w)
     ref = _oracle(w, pk, pv)
     for part in (0, 16):
-        assert_close(out_f64(_run(b, part), "bf16"), ref, "bf16", f"k={k} G={G} D={D} partition {part}")
+        assert_close(out_f64(_run(b, part), "bf16"), ref, "bf16", f"k={k} G={G} D={D} {kv} partition {part}")
 
 
 def test_mixed_draft_lengths_run_both_kernels():

@@ -2,8 +2,10 @@
 
 Prefill rows (sequences with >= 2 new tokens) run on MFMA tiles, 1-token rows on the decode
 kernel.  Bar: bf16 attention within 1e-2 absolute of the oracle (the oracle attends in
-float64 on the exact bf16 cache values, causal mask aligned to the end of the context).
+float64 on the exact cache values -- bf16, or E5M2 codes for an FP8 cache -- causal mask
+aligned to the end of the context).
 """
+import dataclasses
 import zlib
 
 import numpy as np
@@ -32,37 +34,42 @@ def _oracle_rows(w, pk, pv, causal=True):
     return np.concatenate([res[s] for s in range(w.num_seqs)])
 
 
-def test_varlen_workload_full_size():
-    w = make_config(5)
+@pytest.mark.parametrize("kv", ["bf16", "e5m2"])
+def test_varlen_workload_full_size(kv):
+    w = dataclasses.replace(make_config(5), src_dtype="bf16", kv_dtype=kv)
     b = DeviceBatch(w)
     pk, pv = oracle_pools(w)
     ref = _oracle_rows(w, pk, pv)
     for part in (-1, 512):
         got = out_f64(_varlen(b, part), "bf16")
-        err = assert_close(got, ref, "bf16", f"varlen partition {part}")
-        print(f"varlen partition {part}: max abs err {err:.2e}")
+        err = assert_close(got, ref, "bf16", f"varlen {kv} partition {part}")
+        print(f"varlen {kv} partition {part}: max abs err {err:.2e}")
 
 
-def _mixed(seed, G, D, hkv=2):
+def _mixed(seed, G, D, hkv=2, kv="bf16"):
     rng = np.random.default_rng(seed)
     n_new = [2, 3, 17, 31, 32, 33, 100, 1, 1, 64, 5, 1]
     cached = [0, 1, 15, 16, 100, 0, 7, 40, 0, 300, 2, 17]
     lens = np.array(cached) + np.array(n_new)
     order = rng.permutation(len(lens))
     return make_workload(lens[order], q_lens=np.array(n_new)[order], num_q_heads=hkv * G, num_kv_heads=hkv,
-                         head_dim=D, q_dtype="bf16", seed=seed)
+                         head_dim=D, q_dtype="bf16", src_dtype="bf16", kv_dtype=kv, seed=seed)
 
 
-@pytest.mark.parametrize("G,D,causal", [(4, 128, True), (1, 128, True), (2, 128, False), (8, 128, True),
-                                        (16, 128, True), (4, 64, True), (8, 64, False), (16, 64, True)])
-def test_varlen_edge_lengths(G, D, causal):
-    w = _mixed(zlib.crc32(f"vl{G}{D}{causal}".encode()) % 1000, G, D)
+@pytest.mark.parametrize("G,D,causal,kv", [
+    (4, 128, True, "bf16"), (1, 128, True, "bf16"), (2, 128, False, "bf16"), (8, 128, True, "bf16"),
+    (16, 128, True, "bf16"), (4, 64, True, "bf16"), (8, 64, False, "bf16"), (16, 64, True, "bf16"),
+    (4, 128, True, "e5m2"), (1, 128, True, "e5m2"), (2, 128, False, "e5m2"), (16, 128, True, "e5m2"),
+    (8, 64, True, "e5m2"), (16, 64, False, "e5m2"),
+])
+def test_varlen_edge_lengths(G, D, causal, kv):
+    w = _mixed(zlib.crc32(f"vl{G}{D}{causal}".encode()) % 1000, G, D, kv=kv)
     w.causal = causal
     b = DeviceBatch(w)
     pk, pv = oracle_pools(w)
     ref = _oracle_rows(w, pk, pv, causal)
     for part in (0, 16):
-        assert_close(out_f64(_varlen(b, part, causal), "bf16"), ref, "bf16", f"varlen G{G} D{D} causal {causal}")
+        assert_close(out_f64(_varlen(b, part, causal), "bf16"), ref, "bf16", f"varlen {kv} G{G} D{D} causal {causal}")
 
 
 def test_varlen_more_sequences_than_the_ranked_limit():
