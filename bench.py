@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload 1-7 (1-4 decode, 5 packed prefill + decode, 6 speculative verification of 4 tokens, "
-                    "7 decode over an INT8 pool, 8 over a scaled FP8 E4M3 pool)")
+                    "7 decode over an INT8 pool, 8 over a scaled FP8 E4M3 pool, 9 the packed step over an E5M2 "
+                    "pool)")
     ap.add_argument("--replicas", type=int, default=0, help="resident batches to rotate (0: enough for >= 1.2 GB)")
     ap.add_argument("--partition", type=int, default=None, help="partition tokens (default: workload's, else auto)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle timing")
@@ -146,7 +147,10 @@ class VarlenBatch:
         self.tables = torch.from_numpy(w.block_tables).to(dev)
         self.lens = torch.from_numpy(w.context_lens).to(dev)
         shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
-        self.pk = torch.full(shape, POISON_BITS["bf16"], dtype=torch.int16, device=dev).view(torch.bfloat16)
+        if w.kv_dtype == "e5m2":
+            self.pk = torch.full(shape, POISON_BITS["e5m2"], dtype=torch.uint8, device=dev)
+        else:
+            self.pk = torch.full(shape, POISON_BITS["bf16"], dtype=torch.int16, device=dev).view(torch.bfloat16)
         self.pv = self.pk.clone()
         hist = write_plan(w, "cached")
         slots = pa.slot_mapping(torch.from_numpy(hist.cu).to(dev), torch.from_numpy(hist.end_pos).to(dev),
@@ -170,9 +174,10 @@ class VarlenBatch:
         self.resolved = partition if partition >= 0 else pa.auto_partition(n, hkv, g, d, ml)
         P = lambda t: t.data_ptr()
         bf = pa.binding.PA_BF16
+        kd = pa.binding.dtype_code(self.pk)
         self.args_slot = (P(self.slots), P(self.cu_new), P(self.end_new), P(self.tables), mb, n, self.ntok, bs, nb)
         self.args_write = (P(self.knew), P(self.vnew), P(self.pk), P(self.pv), P(self.slots), self.ntok, hkv, d, bs,
-                           nb, bf, bf)
+                           nb, bf, kd)
 
         def varlen_args(s0, s1):
             rows0 = int(w.cu_seqlens_q[s0])
@@ -182,14 +187,14 @@ class VarlenBatch:
             qoff = rows0 * w.num_q_heads * d * 2
             return (P(self.out) + qoff, P(self.q) + qoff, P(self.pk), P(self.pv), P(cu), P(self.lens) + 4 * s0,
                     P(self.tables) + 4 * mb * s0, mb, s1 - s0, int(w.q_lens[s0:s1].sum()), qlen, hkv, g, d, bs, nb,
-                    ml, w.scale, 1, bf, bf, partition, P(self.ws), self.ws.numel())
+                    ml, w.scale, 1, bf, kd, partition, P(self.ws), self.ws.numel())
 
         self._keep = []
         self.args_varlen = varlen_args(0, n)
         self.args_prefill_only = varlen_args(0, n_pre) if n_pre > 0 else None
         self.args_decode_only = varlen_args(n_pre, n) if n_pre < n else None
-        self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * d * 2 * 2
-        self.decode_kv_bytes = int(w.context_lens[n_pre:].astype("int64").sum()) * hkv * d * 2 * 2
+        self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * 2 * row_bytes(w)
+        self.decode_kv_bytes = int(w.context_lens[n_pre:].astype("int64").sum()) * hkv * 2 * row_bytes(w)
         pos = [(int(L) - int(qn) + i + 1) for L, qn in zip(w.context_lens[:n_pre], w.q_lens[:n_pre]) for i in range(qn)]
         self.prefill_flops = 4 * w.num_q_heads * d * int(sum(max(0, x) for x in pos))
 
@@ -255,7 +260,7 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if w0.kv_dtype == "bf16" else f"bf16-q/{w0.kv_dtype}-kv",
         "data": "synthetic",
         "config": {
             "workload": CONFIG_NAMES[args.config],
@@ -633,22 +638,23 @@ def cpu_baseline_varlen(w, budget_s):
     with threadpool_limits(limits=1):
         while t_used < budget_s:
             sel = [(s0 + i) % w.num_seqs for i in range(8)]
-            pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, "bf16", POISON_BITS["bf16"])
+            pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype,
+                                 POISON_BITS[w.kv_dtype])
             pv = pk.copy()
             hist = write_plan(w, "cached", sel)
             hs = oracle.slot_mapping(w.block_tables, hist.counts, hist.end_pos, w.block_size)
-            oracle.cache_write(pk, hist.k, hs, "bf16", "bf16", w.block_size)
-            oracle.cache_write(pv, hist.v, hs, "bf16", "bf16", w.block_size)
+            oracle.cache_write(pk, hist.k, hs, "bf16", w.kv_dtype, w.block_size)
+            oracle.cache_write(pv, hist.v, hs, "bf16", w.kv_dtype, w.block_size)
             new = write_plan(w, "new", sel)
             t0 = time.perf_counter()
             ns = oracle.slot_mapping(w.block_tables, new.counts, new.end_pos, w.block_size)
-            oracle.cache_write(pk, new.k, ns, "bf16", "bf16", w.block_size)
-            oracle.cache_write(pv, new.v, ns, "bf16", "bf16", w.block_size)
-            oracle.paged_varlen(pk, pv, "bf16", q, "bf16", w.cu_seqlens_q, w.block_tables, w.context_lens,
+            oracle.cache_write(pk, new.k, ns, "bf16", w.kv_dtype, w.block_size)
+            oracle.cache_write(pv, new.v, ns, "bf16", w.kv_dtype, w.block_size)
+            oracle.paged_varlen(pk, pv, w.kv_dtype, q, "bf16", w.cu_seqlens_q, w.block_tables, w.context_lens,
                                 w.block_size, w.scale, causal=True, seqs=sel)
             t_used += time.perf_counter() - t0
             done_seqs += len(sel)
-            done_bytes += int(w.context_lens[sel].astype(np.int64).sum()) * w.num_kv_heads * w.head_dim * 4
+            done_bytes += int(w.context_lens[sel].astype(np.int64).sum()) * w.num_kv_heads * 2 * row_bytes(w)
             s0 += 8
     return {
         "value": round(done_bytes / t_used / 1e9, 4),

@@ -42,6 +42,7 @@ CONFIG_NAMES = {
     6: "llama3_8b_spec_verify_k4_bf16",
     7: "llama3_8b_decode_int8_kv",
     8: "llama3_8b_decode_fp8_e4m3_scaled_kv",
+    9: "varlen_prefill_decode_e5m2_kv",
 }
 
 # random streams
@@ -278,6 +279,12 @@ def make_config(idx: int, replica: int = 0) -> Workload:
         lens = rl.integers(256, 4096 + 1, size=128)
         return make_workload(lens, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16",
                              src_dtype="bf16", kv_dtype="int8", seed=seed, name=name)
+    if idx == 9:
+        # the packed prefill + decode step of workload 5 over an E5M2 pool
+        import dataclasses
+
+        base = make_config(5, replica)
+        return dataclasses.replace(base, src_dtype="bf16", kv_dtype="e5m2", name=name)
     if idx == 8:
         # the same batch over a scaled FP8 E4M3 pool
         lens = rl.integers(256, 4096 + 1, size=128)
