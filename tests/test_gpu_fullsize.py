@@ -14,7 +14,7 @@ import torch
 import oracle
 import paged_kv_cache_251_amd as pa
 from gpu_harness import DEV, DeviceBatch, assert_close, canonical, oracle_pools, out_f64
-from workloads import make_config, queries
+from workloads import make_config, make_workload, queries
 
 pytestmark = pytest.mark.gpu
 
@@ -80,3 +80,24 @@ def test_long_context_split_kv_full_size_sampled():
     np.testing.assert_allclose(m[s] + np.log2(l[s]), lse_ref, rtol=0, atol=1e-4)
     assert np.all(m[s] <= om[:, 0, :].T * np.log2(np.e) + 1e-4)
     assert np.abs(o[s] - oo[:, 0].transpose(1, 0, 2)).max() <= 1e-4
+
+
+def test_context_of_128k_tokens():
+    """One sequence of 131072 tokens (8192 blocks, 8 KV heads, 64 query heads) stored in the top
+    of a 2.5 GB pool, so tile byte offsets pass 2^31: the automatic split (256 partitions of
+    512) and a whole-context pass.  The oracle reads the same rows from a compact pool."""
+    import dataclasses
+
+    L = 131072
+    w = make_workload([L, 5], num_q_heads=64, num_kv_heads=8, head_dim=128, q_dtype="bf16", seed=131)
+    off = 66000  # (66000 + 9013 blocks) x 32 KiB per block = 2.46 GB per pool
+    big = dataclasses.replace(w, block_tables=np.where(w.block_tables >= 0, w.block_tables + off, -1).astype(np.int32),
+                              num_blocks=w.num_blocks + off)
+    assert int(big.block_tables.max()) * 8 * 16 * 128 * 2 > 2**31
+    b = DeviceBatch(big)
+    pk, pv = oracle_pools(w)
+    ref = oracle.paged_decode(pk, pv, "bf16", queries(w), "bf16", w.block_tables, w.context_lens, 16, w.scale)
+    assert pa.auto_partition(w.num_seqs, w.num_kv_heads, w.gqa_group, w.head_dim, w.max_context_len) > 0
+    for part in (-1, 0):
+        err = assert_close(out_f64(b.decode(part), "bf16"), ref, "bf16", f"128k context, partition {part}")
+        print(f"128k context partition {part}: max abs err {err:.2e}")
