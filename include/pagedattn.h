@@ -61,8 +61,9 @@
  *
  * Conventions for every entry point
  *   - All pointers are device pointers unless stated; the caller owns every buffer.
- *     The library never allocates or frees device memory, never synchronises, keeps
- *     no state besides a thread-local error string, and is re-entrant.
+ *     The library never allocates or frees device memory and never synchronises.  Its
+ *     state is a thread-local error string and the host objects a caller creates and
+ *     destroys (block managers, schedulers); the attention and cache calls are re-entrant.
  *   - Work is enqueued on `stream`; calls return before the device has finished.
  *   - Scalar arguments and pointer alignment are checked on the host before anything
  *     is enqueued: a bad value returns PA_ERR_INVALID_ARGUMENT, a well-formed but

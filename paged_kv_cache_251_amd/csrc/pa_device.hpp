@@ -185,25 +185,11 @@ __device__ __forceinline__ uint32_t e5m2_cross_pair(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, sel);
 }
 
-// int8 codes -> f16x2 words, exact: with the sign bit of a byte flipped and 0x64 as the upper
-// byte, an f16 holds 1024 + 128 + code; subtracting 1152 (packed f16) leaves the code.
-__device__ __forceinline__ uint32_t i8_finish(uint32_t magic) {
-  const f16x2_t r = __builtin_bit_cast(f16x2_t, magic ^ 0x64806480u) - f16x2_t{(_Float16)1152.0f, (_Float16)1152.0f};
-  return __builtin_bit_cast(uint32_t, r);
-}
-// bytes 0, 1 (lo) or 2, 3 (hi) of w as an f16x2 word
-__device__ __forceinline__ uint32_t i8_pair_lo(uint32_t w) { return i8_finish(__builtin_amdgcn_perm(0u, w, 0x0C010C00u)); }
-__device__ __forceinline__ uint32_t i8_pair_hi(uint32_t w) { return i8_finish(__builtin_amdgcn_perm(0u, w, 0x0C030C02u)); }
-// (byte j of a, byte j of b) as an f16x2 word, low half from a
-template <int J>
-__device__ __forceinline__ uint32_t i8_cross_pair(uint32_t a, uint32_t b) {
-  constexpr uint32_t sel = (uint32_t)J | (0x0Cu << 8) | ((uint32_t)(4 + J) << 16) | (0x0Cu << 24);
-  return i8_finish(__builtin_amdgcn_perm(b, a, sel));
-}
-
-// Biased form for dot products: with wx = w ^ 0x80808080 (each code's sign bit flipped), the
-// upper byte 0x64 comes from the constant operand, and each f16 holds 1152 + code exactly; a
-// dot product against q then carries 1152 * sum(q), which the caller subtracts once.
+// int8 codes -> f16, biased: with the sign bit of a byte flipped and 0x64 as the upper byte, an
+// f16 holds 1024 + 128 + code exactly (1152 + code).
+// Bytes 0, 1 (lo) or 2, 3 (hi) of a word as biased f16: with wx = w ^ 0x80808080 (each code's
+// sign bit flipped) the upper byte 0x64 comes from the constant operand; a dot product against
+// q then carries 1152 * sum(q), which the caller subtracts once.
 __device__ __forceinline__ uint32_t i8_biased_lo(uint32_t wx) { return __builtin_amdgcn_perm(0x64646464u, wx, 0x04010400u); }
 __device__ __forceinline__ uint32_t i8_biased_hi(uint32_t wx) { return __builtin_amdgcn_perm(0x64646464u, wx, 0x04030402u); }
 
