@@ -34,6 +34,15 @@ KV_BYTES = {"f32": 4, "bf16": 2, "e5m2": 1, "int8": 1, "e4m3": 1}
 SCALED = ("int8", "e4m3")  # pools with a float32 scale per (token, KV head) row
 
 
+def launch_stats(ms) -> dict:
+    """Median, min and 90th percentile of per-launch times (ms) in microseconds."""
+    import numpy as np
+
+    us = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median_us": round(float(np.median(us)), 3), "min_us": round(float(us.min()), 3),
+            "p90_us": round(float(np.percentile(us, 90)), 3), "launches": int(us.size)}
+
+
 def row_bytes(w) -> int:
     """Pool bytes of one (token, KV head) row: head_dim elements, plus the float32 scale of an
     INT8 row."""
@@ -231,8 +240,9 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
                 evs[i][1].record(stream)
         stop.record(stream)
         torch.cuda.synchronize()
-        kern = float(np.mean([a.elapsed_time(b) for a, b in evs])) if with_events else None
-        return start.elapsed_time(stop) / args.steps, kern
+        kern = [a.elapsed_time(b) for a, b in evs] if with_events else None
+        timed.last = kern
+        return start.elapsed_time(stop) / args.steps, (float(np.mean(kern)) if with_events else None)
 
     dec = lambda b: check(lib.paged_attention_varlen(*b.args_decode_only, sh), "varlen decode rows")
     pre = lambda b: check(lib.paged_attention_varlen(*b.args_prefill_only, sh), "varlen prefill rows")
@@ -240,6 +250,7 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
         bench_multi_token(args, batches, timed, pre, step, np)
         return
     _, dec_ms = timed(dec, True)
+    dec_list = timed.last
     _, pre_ms = timed(pre, True)
     ms_step, _ = timed(step, False)
     step_bytes = float(np.mean([batches[i % reps].kv_bytes for i in range(args.steps)]))
@@ -288,6 +299,7 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config]),
             "avg_launch_us": round(dec_ms * 1e3, 3),
+            "launch_distribution": launch_stats(dec_list),
             "algorithmic_bytes_per_launch": int(dec_bytes),
         },
         "prefill_mfma": {
@@ -314,6 +326,7 @@ def bench_multi_token(args, batches, timed, call, step, np):
     w0 = batches[0].w
     reps = len(batches)
     _, call_ms = timed(call, True)
+    call_list = timed.last
     ms_step, _ = timed(step, False)
     step_bytes = float(np.mean([batches[i % reps].kv_bytes for i in range(args.steps)]))
     flops = float(np.mean([batches[i % reps].prefill_flops for i in range(args.steps)]))
@@ -358,6 +371,7 @@ def bench_multi_token(args, batches, timed, call, step, np):
             "frac": round(call_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config]),
             "avg_launch_us": round(call_ms * 1e3, 3),
+            "launch_distribution": launch_stats(call_list),
             "algorithmic_bytes_per_launch": int(step_bytes),
             "mfma_tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
         },
@@ -518,6 +532,7 @@ def main():
             "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "avg_launch_us": round(kern_avg * 1e3, 3),
+            "launch_distribution": launch_stats(kern_ms),
             "algorithmic_bytes_per_launch": int(step_bytes),
         },
         "cpu_baseline": cpu,
