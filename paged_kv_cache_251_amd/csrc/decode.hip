@@ -677,13 +677,18 @@ static int device_cus() {
   return cus;
 }
 
-// Work-groups of `kernel` (block of `threads`) that one CU holds at once (cached per kernel).
-template <typename K>
-static int resident_per_cu(K kernel, int threads) {
+// Work-groups of one instantiation of the decode kernel that one CU holds at once (cached per
+// instantiation: every instantiation has the same function type, so the cache is keyed by the
+// template arguments, not by the pointer's type).
+template <int KV, int D, int G, int W>
+static int resident_per_cu() {
   static std::atomic<int> cache{0};
   int c = cache.load(std::memory_order_relaxed);
   if (c > 0) return c;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, kernel, threads, 0) != hipSuccess || c <= 0) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&c, decode_partition_kernel<KV, D, G, W>, 64 * W, 0) !=
+          hipSuccess ||
+      c <= 0)
+    return 0;
   cache.store(c, std::memory_order_relaxed);
   return c;
 }
@@ -701,7 +706,7 @@ static hipError_t launch_parts_kv_d_g(const DecodeParams& p, int num_seqs, hipSt
     if (p.longest_first) {
       const long long units = (long long)num_seqs * p.num_kv_heads;
       const int cus = device_cus();
-      if (cus > 0 && units <= (long long)cus * resident_per_cu(kernel, 64 * W)) q.snake = cus;
+      if (cus > 0 && units <= (long long)cus * resident_per_cu<KV, D, G, W>()) q.snake = cus;
     }
     hipLaunchKernelGGL(kernel, grid, dim3(64 * W), 0, stream, q);
   } else {

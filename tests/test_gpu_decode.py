@@ -146,7 +146,9 @@ def test_block_permutation_is_bit_identical(idx):
                            moved.view(torch.int16 if w.q_dtype == "bf16" else torch.int32))
 
 
-EDGE_LENS = [0, 1, 2, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000]
+# Per wave of a 4-wave whole-context pass these give 0 to 16 tiles: every peeled tail of the
+# prefetch loop (100 and 150: two and three tiles on the first waves)
+EDGE_LENS = [0, 1, 2, 15, 16, 17, 100, 150, 255, 256, 257, 511, 512, 513, 700, 1000]
 
 
 @pytest.mark.parametrize("dtype,D,hkv,G", [
