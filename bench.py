@@ -2,8 +2,8 @@
 """Paged decode attention benchmark on one MI355X.
 
 One step = the whole decode path for one batch: slot mapping of each sequence's
-newest token, the cache write of its K/V row (cast to E5M2 for an fp8 cache),
-the paged attention partition pass and, when contexts are split, the reduce
+newest token, the cache write of its K/V row (cast to E5M2 for an fp8 cache,
+quantised with a per-row scale for an INT8 or E4M3 cache), the paged attention partition pass and, when contexts are split, the reduce
 pass.  The timed step runs these as one fused launch
 (paged_attention_decode_append; plus the reduce kernel when split); the same
 step as three separate calls (slot mapping, kv_cache_write, decode) is timed
@@ -102,8 +102,9 @@ class Batch:
             ints = {"f32": torch.int32, "bf16": torch.int16, "e5m2": torch.uint8}[w.kv_dtype]
             store = {"f32": torch.float32, "bf16": torch.bfloat16, "e5m2": torch.uint8}[w.kv_dtype]
             self.pk = torch.full(shape, POISON_BITS[w.kv_dtype], dtype=ints, device=dev).view(store)
-        # a scaled pool is written by the cache write's quantiser (no fused append)
-        self.fused = w.kv_dtype not in SCALED
+        # every pool kind but INT8 takes the fused append (an E4M3 pool's new row is quantised in the
+        # kernel); an INT8 pool is written by the cache write's quantiser
+        self.fused = w.kv_dtype != "int8"
         self.pv = self.pk.clone()
         hist = write_plan(w, "cached")
         slots = pa.slot_mapping(torch.from_numpy(hist.cu).to(dev), torch.from_numpy(hist.end_pos).to(dev),
@@ -513,7 +514,8 @@ def main():
             "context_lens": f"{int(w0.context_lens.min())}..{int(w0.context_lens.max())}",
             "partition_tokens": batches[0].resolved,
             "resident_batches": reps,
-            "step": ("one launch: slot mapping + cache write of the newest token + decode attention" if fused else
+            "step": (("one launch: slot mapping + " + ("quantising " if w0.kv_dtype in SCALED else "") +
+                      "cache write of the newest token + decode attention") if fused else
                      f"slot mapping + {w0.kv_dtype.upper()} cache write (quantise) of the newest token + decode "
                      "attention") +
                     (" (split-KV partitions) + the separate reduce kernel" if batches[0].split else ""),
@@ -528,7 +530,7 @@ def main():
                      (" + separate reduce kernel" if batches[0].split else "")},
         "wall_s": round(wall, 4),
         "roofline": {
-            "kernel": "decode_partition_kernel" + (" (append mode)" if fused else f" ({w0.kv_dtype.upper()} pool)"),
+            "kernel": "decode_partition_kernel" + (" (append mode" if fused else " (") + f", {w0.kv_dtype.upper()} pool)",
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,

@@ -76,8 +76,8 @@
  *     [0, min(max_context_len, max_blocks_per_seq * block_size)].  Results for such
  *     inputs are unspecified but no access leaves the buffers described here.
  *   - Supported now: block_size 16; head_dim 64 or 128; gqa_group 1, 2, 4, 8 or 16;
- *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), and (BF16, INT8) and
- *     (BF16, FP8_E4M3) for the decode calls without append; packed (varlen) batches take
+ *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, FP8_E4M3), and
+ *     (BF16, INT8) for the decode calls without append; packed (varlen) batches take
  *     (BF16, BF16) and (BF16, FP8_E5M2).
  */
 #ifndef PAGEDATTN_H
@@ -258,12 +258,13 @@ pa_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens
  * The newest token of sequence s sits at position L-1 (L = context_lens[s], which counts
  * it).  Its rows key[s], value[s] ([num_kv_heads][head_dim], q_dtype, dense, 16-byte
  * aligned) are stored at slot block_tables[s][(L-1)/B]*B + (L-1)%B of the pools (cast to
- * E5M2 when kv_dtype is FP8_E5M2, exactly as kv_cache_write casts), and the attention is
- * paged_attention_decode over all L tokens.  The result is bit-identical to
- * paged_kv_slot_mapping + kv_cache_write + paged_attention_decode with the same
- * partition size.  A sequence with L = 0 appends nothing.  A slot whose table entry is
- * outside [0, num_blocks) is not written.  INT8 and FP8_E4M3 pools are not supported here
- * (PA_ERR_UNSUPPORTED): write their rows with kv_cache_write.
+ * E5M2 when kv_dtype is FP8_E5M2, quantised to codes and a row scale when it is FP8_E4M3,
+ * exactly as kv_cache_write does), and the attention is paged_attention_decode over all L
+ * tokens.  The result, pools and output, is bit-identical to paged_kv_slot_mapping +
+ * kv_cache_write + paged_attention_decode with the same partition size.  A sequence with
+ * L = 0 appends nothing.  A slot whose table entry is outside [0, num_blocks) is not
+ * written.  INT8 pools are not supported here (PA_ERR_UNSUPPORTED): write their rows with
+ * kv_cache_write.
  *
  * flags: PA_APPEND_SKIP_REDUCE -- run only the streaming pass; the caller then runs
  *        paged_attention_decode_reduce (same arguments) when a sequence is split.

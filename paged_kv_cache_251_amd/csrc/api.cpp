@@ -384,8 +384,8 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
                                   max_context_len, scale, q_dtype, kv_dtype, partition_size, workspace,
                                   workspace_bytes, true);
   if (st != PA_OK) return st;
-  if (scaled_dtype(kv_dtype))
-    return fail(PA_ERR_UNSUPPORTED, "%s: INT8 / FP8_E4M3 pools are written by kv_cache_write (no fused append)", fn);
+  if (kv_dtype == PA_INT8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: INT8 pools are written by kv_cache_write (no fused append)", fn);
   if (num_seqs == 0) return ok();
   if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "%s: null key/value row pointer", fn);
   if (!aligned(key, 16) || !aligned(value, 16))

@@ -109,7 +109,6 @@ __global__ __launch_bounds__(256) void cache_write_q8_kernel(const uint4* __rest
                                                              int32_t num_kv_heads, int32_t num_blocks) {
   constexpr int LPR = D / 8;  // lanes per row; divides 64, so a row never straddles waves
   constexpr int TILE = TileStride<KV, D>::value;
-  constexpr float RANGE = KV == KV_I8 ? 127.0f : 448.0f;  // largest code magnitude
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)num_tokens * num_kv_heads * LPR;
   if (i >= total) return;  // total is a multiple of LPR: a row's lanes leave together
@@ -129,27 +128,17 @@ __global__ __launch_bounds__(256) void cache_write_q8_kernel(const uint4* __rest
     for (int k = 0; k < 4; ++k) {
       x[2 * k] = bf16lo(words[k]);
       x[2 * k + 1] = bf16hi(words[k]);
-      const int a0 = (int)(words[k] & 0x7FFFu), a1 = (int)((words[k] >> 16) & 0x7FFFu);
-      key_max = max(key_max, max(a0 > 0x7F80 ? -1 : a0, a1 > 0x7F80 ? -1 : a1));
+      key_max = max(key_max, max(bf16_mag_key(words[k]), bf16_mag_key(words[k] >> 16)));
     }
 #pragma unroll
     for (int off = LPR / 2; off >= 1; off >>= 1) key_max = max(key_max, __shfl_xor(key_max, off));
-    const float amax = key_max < 0 ? __builtin_nanf("") : as_f32((uint32_t)key_max << 16);
-    const float inv = amax > 0.f ? RANGE / amax : 0.f;
+    const float amax = q8_amax(key_max);
+    const float inv = q8_inv<KV>(amax);
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t code;
-      if constexpr (KV == KV_I8) {
-        const float q = rintf(x[k] * inv);
-        code = (uint32_t)(q != q ? -127 : (int)fminf(fmaxf(q, -127.f), 127.f)) & 0xFFu;
-      } else {
-        code = f32_to_e4m3_sat(x[k] * inv);
-      }
-      packed[k >> 2] |= code << (8 * (k & 3));
-    }
+    for (int k = 0; k < 8; ++k) packed[k >> 2] |= q8_code<KV>(x[k], inv) << (8 * (k & 3));
     *reinterpret_cast<uint2*>(pool + tile + (size_t)r * D + (size_t)c * 8) = make_uint2(packed[0], packed[1]);
-    if (c == 0) *reinterpret_cast<float*>(pool + tile + 16 * D + 4 * (4 * (r & 3) + (r >> 2))) = amax / RANGE;
+    if (c == 0) *reinterpret_cast<float*>(pool + tile + q8_scale_offset<D>(r)) = amax / Q8Range<KV>::value;
   };
   quantize(key[i], key_cache);
   quantize(value[i], value_cache);

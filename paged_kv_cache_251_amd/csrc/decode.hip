@@ -145,11 +145,14 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
   // b_new then comes from the new row instead of the cache (no read-after-write inside
   // the launch).  Lane (row, col) keeps columns col*EPL .. col*EPL+EPL-1 in cache format.
   const int pos_new = L - 1;
-  const bool appending = !Scaled<KV>::value && p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
+  // (INT8 pools do not append: the kernel is held to 128 VGPRs, and the splice's registers would
+  // spill inside the tile loop)
+  const bool appending = KV != KV_I8 && p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
   const int b_new = appending ? pos_new / 16 : -1;
   const int r_new = pos_new & 15;
   uint32_t knew[NDW], vnew[NDW];
-  uint32_t kraw[KV == KV_E5M2 ? 2 * NDW : 1], vraw[KV == KV_E5M2 ? 2 * NDW : 1];
+  constexpr bool RAW = KV == KV_E5M2 || KV == KV_E4M3;  // the new row arrives as bf16 and is cast
+  uint32_t kraw[RAW ? 2 * NDW : 1], vraw[RAW ? 2 * NDW : 1];
   if (appending) {
     const size_t roff = ((size_t)s * p.num_kv_heads + g) * D + (size_t)col * EPL;  // element offset
     if constexpr (KV == KV_F32) {
@@ -158,16 +161,36 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
     } else if constexpr (KV == KV_BF16) {
       load_dw<NDW>(knew, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
       load_dw<NDW>(vnew, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
-    } else if constexpr (KV == KV_E5M2) {  // (an INT8 pool never appends)
+    } else if constexpr (RAW) {  // E5M2, E4M3: bf16 rows
       load_dw<2 * NDW>(kraw, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
       load_dw<2 * NDW>(vraw, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
     }
   }
   // Once the first tile is in flight: cast the new row to the cache type (bf16 -> E5M2 is
-  // the cache write's own cast) and store it at its slot.
+  // the cache write's own cast; E4M3 rows are quantised with the cache write's rule, the row's
+  // amax reduced over the 16 lanes of a DPP row) and store it at its slot.
+  float kscale = 0.f, vscale = 0.f;  // E4M3: the new rows' scales
   auto finish_append = [&]() {
     if (!appending) return;
-    if constexpr (KV == KV_E5M2) {
+    if constexpr (KV == KV_E4M3) {
+      auto quantize_row = [&](const uint32_t(&raw)[2 * NDW], uint32_t(&codes)[NDW]) -> float {
+        int key_max = -1;
+#pragma unroll
+        for (int j = 0; j < 2 * NDW; ++j) key_max = max(key_max, max(bf16_mag_key(raw[j]), bf16_mag_key(raw[j] >> 16)));
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) key_max = max(key_max, __shfl_xor(key_max, off));
+        const float amax = q8_amax(key_max);
+        const float inv = q8_inv<KV>(amax);
+#pragma unroll
+        for (int j = 0; j < NDW; ++j)
+          codes[j] = q8_code<KV>(bf16lo(raw[2 * j]), inv) | (q8_code<KV>(bf16hi(raw[2 * j]), inv) << 8) |
+                     (q8_code<KV>(bf16lo(raw[2 * j + 1]), inv) << 16) |
+                     (q8_code<KV>(bf16hi(raw[2 * j + 1]), inv) << 24);
+        return amax / Q8Range<KV>::value;
+      };
+      kscale = quantize_row(kraw, knew);
+      vscale = quantize_row(vraw, vnew);
+    } else if constexpr (KV == KV_E5M2) {
 #pragma unroll
       for (int j = 0; j < NDW; ++j) {
         knew[j] = bf16_to_e5m2(kraw[2 * j] & 0xFFFFu) | (bf16_to_e5m2(kraw[2 * j] >> 16) << 8) |
@@ -178,7 +201,16 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
     }
     const int phys = load_invariant(p.block_tables + (size_t)s * p.max_blocks_per_seq + b_new);
     if (wave == 0 && row == 0 && phys >= 0 && phys < p.num_blocks) {
-      const size_t dst = ((((size_t)phys * p.num_kv_heads + g) * 16 + r_new) * D + (size_t)col * EPL) * SZ;
+      const size_t tile = ((size_t)phys * p.num_kv_heads + g) * T::TILE;
+      const size_t dst = tile + ((size_t)r_new * D + (size_t)col * EPL) * SZ;
+      if constexpr (KV == KV_E4M3) {
+        if (col == 0) {
+          *reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + tile + q8_scale_offset<D>(r_new)) =
+              kscale;
+          *reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p.value_cache_w) + tile + q8_scale_offset<D>(r_new)) =
+              vscale;
+        }
+      }
       uint32_t* kc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + dst);
       uint32_t* vc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.value_cache_w) + dst);
 #pragma unroll
@@ -270,6 +302,10 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
         for (int j = 0; j < NDW; ++j) {
           kd[i][j] = mine ? knew[j] : kd[i][j];
           vd[i][j] = mine ? vnew[j] : vd[i][j];
+        }
+        if constexpr (KV == KV_E4M3) {
+          ks[i] = mine ? as_u32(kscale) : ks[i];
+          vs[i] = mine ? as_u32(vscale) : vs[i];
         }
       }
     }

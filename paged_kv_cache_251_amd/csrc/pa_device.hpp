@@ -229,6 +229,45 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_sat(float y) {
   return sign | (q > 0x7Eu ? 0x7Eu : q);
 }
 
+// Scaled 8-bit rows (INT8, E4M3): one float32 scale per (token, KV head) row, scale = amax / RANGE
+// and code = Q(x * RANGE / amax), where amax is the largest magnitude of the row's bf16 elements
+// with NaN ignored.  Both the cache write and the fused append use these, so their bytes agree.
+template <int KV>
+struct Q8Range {
+  static constexpr float value = KV == KV_I8 ? 127.0f : 448.0f;  // largest code magnitude
+};
+// Order key of one bf16 element's magnitude: its 15-bit pattern, or -1 for NaN; the row's
+// largest key gives amax (all NaN: key -1, amax NaN).
+__device__ __forceinline__ int bf16_mag_key(uint32_t bits16) {
+  const int a = (int)(bits16 & 0x7FFFu);
+  return a > 0x7F80 ? -1 : a;
+}
+__device__ __forceinline__ float q8_amax(int key_max) {
+  return key_max < 0 ? __builtin_nanf("") : as_f32((uint32_t)key_max << 16);
+}
+template <int KV>
+__device__ __forceinline__ float q8_inv(float amax) {
+  return amax > 0.f ? Q8Range<KV>::value / amax : 0.f;
+}
+// code byte of one element (INT8: nearest even, clamped to [-127, 127], NaN -> -127; E4M3: the
+// saturating nearest-even encoder)
+template <int KV>
+__device__ __forceinline__ uint32_t q8_code(float x, float inv) {
+  if constexpr (KV == KV_I8) {
+    const float q = rintf(x * inv);
+    return (uint32_t)(q != q ? -127 : (int)fminf(fmaxf(q, -127.f), 127.f)) & 0xFFu;
+  } else {
+    return f32_to_e4m3_sat(x * inv);
+  }
+}
+// byte offset, inside a scaled tile of head_dim D, of the scale of token r of the block: token
+// r's scale sits at index 4(r mod 4) + r/4, so a lane of DPP row q reads the scales of its
+// tokens q, q+4, q+8, q+12 with one 16-byte load
+template <int D>
+__device__ __forceinline__ int q8_scale_offset(int r) {
+  return 16 * D + 4 * (4 * (r & 3) + (r >> 2));
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
                                          false);

@@ -109,10 +109,17 @@ def test_cache_write_rejects_bad_arguments_on_host(lib):
 
 
 def test_int8_pool_is_rejected_where_unsupported(lib):
-    # the fused append writes rows in the query dtype's cast; an INT8 pool is written by kv_cache_write
+    # the fused append: an INT8 pool is written by kv_cache_write; an FP8_E4M3 pool takes bf16
+    # queries and rows, and with them gets as far as the row pointers (checked on the host)
     app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
                                             64, 0.1, 1, 3, 0, 0, None, 0, None)
     assert app == 2 and b"INT8" in lib.pa_last_error()
+    app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
+                                            64, 0.1, 0, 4, 0, 0, None, 0, None)
+    assert app == 2  # f32 queries
+    app = lib.paged_attention_decode_append(FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
+                                            64, 0.1, 1, 4, 0, 0, None, 0, None)
+    assert app == 1 and b"key/value row" in lib.pa_last_error()
     for kd in (0, 3, 4):  # packed batches take bf16 or FP8_E5M2 pools only
         var = lib.paged_attention_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 2, 2, 2, 128, 16, 8, 64,
                                          0.1, 1, 1, kd, 0, None, 0, None)
@@ -120,9 +127,6 @@ def test_int8_pool_is_rejected_where_unsupported(lib):
     cp = lib.paged_kv_copy_blocks(FAKE, FAKE, FAKE, 1, 2, 128, 32, 8, 3, None)
     assert cp == 2
     for kd in (3, 4):  # INT8, FP8_E4M3
-        app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16,
-                                                8, 64, 0.1, 1, kd, 0, 0, None, 0, None)
-        assert app == 2
         assert lib.paged_kv_copy_blocks(FAKE, FAKE, FAKE, 1, 2, 128, 32, 8, kd, None) == 2
 
 

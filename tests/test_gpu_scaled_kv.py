@@ -203,3 +203,41 @@ def test_scaled_decode_full_size_sampled(kind):
         out = out_f64(b.decode(part), "bf16")[sel]
         err = assert_close(out, ref, "bf16", f"{kind} full size partition {part}")
         print(f"{kind} full size partition {part}: max abs err {err:.2e}")
+
+
+# ---------------------------------------------------------------- fused append on scaled pools
+@pytest.mark.parametrize("kind", ["e4m3"])
+@pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 4), (64, 16)])
+def test_scaled_append_is_bit_identical_to_write_then_decode(kind, D, G):
+    """paged_attention_decode_append quantises each sequence's newest K/V row in the kernel (FP8
+    E4M3 pools; INT8 pools are written by kv_cache_write): the pools it leaves and its output equal,
+    byte for byte, the quantising kv_cache_write followed by the decode, and both match the
+    oracle's codes, scales and attention."""
+    from workloads import STORAGE, seq_kv
+
+    w = make_workload([1, 2, 16, 17, 32, 33, 300, 513, 0], num_q_heads=2 * G, num_kv_heads=2, head_dim=D,
+                      q_dtype="bf16", src_dtype="bf16", kv_dtype=kind,
+                      seed=zlib.crc32(f"app{kind}{D}{G}".encode()) % 1000)
+    o = oracle_int8_pools(w)
+    ref = oracle.paged_decode(o["k"][3], o["v"][3], "f64", queries(w), "bf16", w.block_tables, w.context_lens,
+                              16, w.scale)
+    kn = np.zeros((w.num_seqs, w.num_kv_heads, w.head_dim), STORAGE["bf16"])
+    vn = np.zeros_like(kn)
+    for s in range(w.num_seqs):
+        if w.context_lens[s] > 0:
+            ks, vs = seq_kv(w, s)
+            kn[s], vn[s] = ks[-1], vs[-1]
+    k = to_device(kn, "bf16")
+    v = to_device(vn, "bf16")
+    for part in (0, 256):
+        a = DeviceBatch(w, phases=("cached",))
+        b = DeviceBatch(w, phases=("cached",))
+        a.write("new")
+        out_sep = a.decode(part)
+        out_fused = pa.paged_attention_decode_append(b.q, k, v, b.pk, b.pv, b.tables, b.lens, w.max_context_len,
+                                                     w.scale, partition_size=part)
+        assert torch.equal(out_sep.view(torch.int16), out_fused.view(torch.int16)), f"{kind} partition {part}"
+        assert torch.equal(a.pk.view(torch.uint8), b.pk.view(torch.uint8))
+        assert torch.equal(a.pv.view(torch.uint8), b.pv.view(torch.uint8))
+        _check_pools_match(b, w, o)
+        assert_close(out_f64(out_fused, "bf16"), ref, "bf16", f"{kind} append D{D} G{G} partition {part}")
