@@ -1,0 +1,144 @@
+"""Work-order arithmetic of the kernels, replayed on the CPU.
+
+The decode and prefill kernels each turn a work-group index into a work unit with integer
+steps that every work-group repeats on its own (decode: rank the sequences by length, take the
+unit of its rank, mirror every second lap when the grid is resident; prefill: count the query
+tiles above a key, binary-search the key of its rank, resolve ties by sequence).  The GPU parity
+tests show that every output row gets computed; these tests replay the same integer steps in
+Python on many random batches and check the properties the order is meant to have: the grid maps
+onto the units one to one, in the intended order, and the host's grid bound covers every unit.
+"""
+import numpy as np
+import pytest
+
+
+# ---------------------------------------------------------------- decode: longest first, snake
+def decode_unit(j, lens, hkv, snake):
+    """(sequence, KV head) of work-group j = z * hkv + x, as the decode kernel computes it."""
+    n = len(lens)
+    order = [0] * n
+    for t in range(n):
+        r = sum(1 for u in range(n) if lens[u] > lens[t] or (lens[u] == lens[t] and u < t))
+        order[r] = t
+    if snake > 0:
+        lap, pos = divmod(j, snake)
+        lap_len = min(snake, n * hkv - lap * snake)
+        if lap & 1:
+            j = lap * snake + (lap_len - 1 - pos)
+    return order[j // hkv], j % hkv
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_order_is_a_bijection_longest_first(seed):
+    rng = np.random.default_rng(seed)
+    n = int(rng.integers(1, 70))
+    hkv = int(rng.choice([1, 2, 3, 8]))
+    lens = rng.integers(0, 40, size=n).tolist()  # many ties
+    for snake in (0, 7, 16, 256):
+        units = [decode_unit(j, lens, hkv, snake) for j in range(n * hkv)]
+        assert sorted(units) == [(s, g) for s in range(n) for g in range(hkv)]
+        if snake == 0:  # dispatch order: lengths never increase, ties by sequence index
+            keys = [(-lens[s], s) for s, _ in units]
+            assert keys == sorted(keys)
+        else:  # each lap holds the same units as the plain order's lap (mirrored on odd laps)
+            plain = [decode_unit(j, lens, hkv, 0) for j in range(n * hkv)]
+            for lap0 in range(0, n * hkv, snake):
+                assert sorted(units[lap0:lap0 + snake]) == sorted(plain[lap0:lap0 + snake])
+
+
+def test_snake_pairs_long_and_short_contexts_on_a_cu():
+    # work-groups i and i + snake share a CU when the grid is resident: rank i pairs with the
+    # mirrored rank, so every CU gets one of the longest and one of the shortest contexts
+    lens = list(range(100, 0, -1))  # 100 sequences, already longest first
+    units = [decode_unit(j, lens, 1, 50) for j in range(100)]
+    sums = [lens[units[i][0]] + lens[units[i + 50][0]] for i in range(50)]
+    assert max(sums) == min(sums) == 101
+
+
+# ---------------------------------------------------------------- prefill: rank -> unit
+def prefill_schedule(cu_q, context_lens, tokw):
+    """Unit (sequence, query tile) of every rank, or None for a spare work-group, as the prefill
+    kernel computes it; and the host's bound on the number of ranks."""
+    nseq = len(context_lens)
+    q = np.diff(cu_q)
+    comp = [(int(context_lens[s] - q[s]), int(q[s]), s) for s in range(nseq) if q[s] >= 2]
+
+    def count_gt(k):
+        c = 0
+        for base, nn, _ in comp:
+            x = k - base
+            t = (nn + tokw - 1) // tokw
+            c += t if x < 0 else (0 if x >= nn else t - x // tokw)
+        return c
+
+    total_q = int(cu_q[-1])
+    chunks = min(nseq, total_q // 2)
+    tiles_per_seq = (int(q.max()) + tokw - 1) // tokw if nseq else 0
+    bound = min((total_q + chunks * (tokw - 1)) // tokw, tiles_per_seq * nseq)
+
+    out = []
+    for pair in range(bound):
+        if not comp:
+            out.append(None)
+            continue
+        klo = min(b + 1 for b, _, _ in comp)
+        khi = max(b + nn for b, nn, _ in comp)
+        if pair >= count_gt(klo - 1):
+            out.append(None)
+            continue
+        while klo < khi:
+            mid = klo + (khi - klo + 1) // 2
+            if count_gt(mid - 1) > pair:
+                klo = mid
+            else:
+                khi = mid - 1
+        rank_in_key = pair - count_gt(klo)
+        seen = 0
+        unit = None
+        for base, nn, s in comp:
+            x = klo - base
+            has = x == nn or (tokw <= x < nn and x % tokw == 0)
+            if has:
+                if seen == rank_in_key:
+                    tt = (nn + tokw - 1) // tokw - 1 if x == nn else x // tokw - 1
+                    unit = (s, tt, klo)
+                    break
+                seen += 1
+        out.append(unit)
+    return out, bound
+
+
+def _random_packed(rng):
+    nseq = int(rng.integers(1, 40))
+    q = np.where(rng.random(nseq) < 0.5, 1, rng.integers(2, 300, size=nseq))
+    q[rng.random(nseq) < 0.2] = 0  # sequences with no row this step
+    cached = rng.integers(0, 500, size=nseq)
+    cached[rng.random(nseq) < 0.3] = 0
+    lens = cached + q
+    # ties on purpose: equal chunks at equal offsets
+    if nseq >= 4:
+        q[1], lens[1] = q[0], lens[0]
+        q[3], lens[3] = q[2], lens[2]
+    cu = np.concatenate([[0], np.cumsum(q)]).astype(np.int64)
+    return cu, lens.astype(np.int64)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_order_is_a_bijection_in_descending_key(G, seed):
+    rng = np.random.default_rng(100 * G + seed)
+    cu, lens = _random_packed(rng)
+    tokw = 128 // G
+    got, bound = prefill_schedule(cu, lens, tokw)
+    q = np.diff(cu)
+    want = {(s, t) for s in range(len(lens)) if q[s] >= 2 for t in range((q[s] + tokw - 1) // tokw)}
+    units = [u for u in got if u is not None]
+    assert sorted((s, t) for s, t, _ in units) == sorted(want)  # every unit once, none twice
+    assert len(want) <= bound  # the host's grid bound covers every unit
+    n_units = len(units)
+    assert all(u is not None for u in got[:n_units]) and all(u is None for u in got[n_units:])  # spares last
+    keys = [k for _, _, k in units]
+    assert keys == sorted(keys, reverse=True)  # longest (most keys seen) first
+    for s, t, k in units:  # the key is the keys seen by the tile's last row
+        base = int(lens[s] - q[s])
+        assert k == base + min(int(q[s]), (t + 1) * tokw)
