@@ -65,6 +65,44 @@ __device__ __forceinline__ uint32_t bcast_head_u32(uint32_t v, int h) {
   return v;
 }
 
+// Longest-first unit of this work-group (grid x = KV head, z = rank).  Every work-group ranks the
+// sequences by context length (ties by index) and takes the (sequence, head) unit of its rank.
+// In a packed batch (cu_q non-null) the sequences that are not 1-token rows rank last (their
+// work-groups return at once), and the number of sequences that take part is counted, so that the
+// snake order -- rank order mirrored on every second lap of `snake` work-groups, pairing long and
+// short contexts on each CU -- is applied whenever their units fit the `resident` work-groups,
+// whatever the batch's other rows.  Every thread of the work-group must call it (it synchronises).
+template <int THREADS>
+__device__ __forceinline__ int2 decode_unit_order(const int32_t* context_lens, const int32_t* cu_q, int n, int hkv,
+                                                 int snake, int resident, int* len, int* order, int* active) {
+  for (int t = threadIdx.x; t < n; t += THREADS) {
+    int L = load_invariant(context_lens + t);
+    if (cu_q != nullptr && load_invariant(cu_q + t + 1) - load_invariant(cu_q + t) != 1) L = -1;
+    len[t] = L;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += THREADS) {
+    const int lt = len[t];
+    int r = 0, inactive = 0;
+    for (int u = 0; u < n; ++u) {
+      const int lu = len[u];
+      r += (lu > lt) | ((lu == lt) & (u < t));
+      inactive += lu < 0;
+    }
+    order[r] = t;
+    if (t == 0) *active = n - inactive;
+  }
+  __syncthreads();
+  int j = blockIdx.z * hkv + blockIdx.x;
+  const int total = *active * hkv;
+  if (snake > 0 && total <= resident && j < total) {
+    const int lap = j / snake, pos = j % snake;
+    const int lap_len = min(snake, total - lap * snake);
+    if (lap & 1) j = lap * snake + (lap_len - 1 - pos);
+  }
+  return make_int2(order[j / hkv], j % hkv);
+}
+
 template <int KV, int D, int G>
 struct DecodeTile {
   static constexpr int SZ = KvBytes<KV>::value;
@@ -101,7 +139,9 @@ __global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_E
   if (p.longest_first) {
     __shared__ int sm_len[kMaxRankedSeqs];
     __shared__ int sm_order[kMaxRankedSeqs];
-    const int2 u = longest_first_unit<64 * W>(p.context_lens, gridDim.z, gridDim.x, p.snake, sm_len, sm_order);
+    __shared__ int sm_active;
+    const int2 u = decode_unit_order<64 * W>(p.context_lens, p.cu_q, gridDim.z, gridDim.x, p.snake, p.resident, sm_len,
+                                             sm_order, &sm_active);
     s = u.x;
     g = u.y;
   }
@@ -739,10 +779,14 @@ static hipError_t launch_parts_kv_d_g(const DecodeParams& p, int num_seqs, hipSt
     auto kernel = decode_partition_kernel<KV, D, G, W>;
     DecodeParams q = p;
     q.snake = 0;
-    if (p.longest_first) {
-      const long long units = (long long)num_seqs * p.num_kv_heads;
+    q.resident = 0;
+    if (p.longest_first) {  // the kernel applies the snake order when its units fit the resident grid
       const int cus = device_cus();
-      if (cus > 0 && units <= (long long)cus * resident_per_cu<KV, D, G, W>()) q.snake = cus;
+      const int per_cu = resident_per_cu<KV, D, G, W>();
+      if (cus > 0 && per_cu > 0) {
+        q.snake = cus;
+        q.resident = cus * per_cu;
+      }
     }
     hipLaunchKernelGGL(kernel, grid, dim3(64 * W), 0, stream, q);
   } else {

@@ -45,6 +45,9 @@ struct DecodeParams {
   // rank order is reversed on every second lap of this length, pairing long contexts with
   // short ones on each CU.  0: plain rank order.
   int32_t snake;
+  // Decode kernel: work-groups resident at once (from the occupancy); the snake order is applied
+  // when the units of the sequences that take part fit in it (the kernel counts them).
+  int32_t resident;
   int32_t causal;  // packed (varlen) batches: mask aligned to the end of each context
   // Prefill kernel: number of sequences to rank into the longest-first unit order (the grid
   // is then one-dimensional); 0: natural three-dimensional order.

@@ -13,16 +13,22 @@ import pytest
 
 
 # ---------------------------------------------------------------- decode: longest first, snake
-def decode_unit(j, lens, hkv, snake):
-    """(sequence, KV head) of work-group j = z * hkv + x, as the decode kernel computes it."""
+def decode_unit(j, lens, hkv, snake, resident=None, q_counts=None):
+    """(sequence, KV head) of work-group j = z * hkv + x, as the decode kernel computes it: in a
+    packed batch (q_counts given) the sequences that are not 1-token rows rank last, and the
+    snake order applies when the taking-part units fit the resident work-groups."""
     n = len(lens)
+    key = [(-1 if q_counts is not None and q_counts[t] != 1 else lens[t]) for t in range(n)]
     order = [0] * n
     for t in range(n):
-        r = sum(1 for u in range(n) if lens[u] > lens[t] or (lens[u] == lens[t] and u < t))
+        r = sum(1 for u in range(n) if key[u] > key[t] or (key[u] == key[t] and u < t))
         order[r] = t
-    if snake > 0:
+    total = (n - sum(1 for k in key if k < 0)) * hkv
+    if resident is None:
+        resident = n * hkv
+    if snake > 0 and total <= resident and j < total:
         lap, pos = divmod(j, snake)
-        lap_len = min(snake, n * hkv - lap * snake)
+        lap_len = min(snake, total - lap * snake)
         if lap & 1:
             j = lap * snake + (lap_len - 1 - pos)
     return order[j // hkv], j % hkv
@@ -46,13 +52,29 @@ def test_decode_order_is_a_bijection_longest_first(seed):
                 assert sorted(units[lap0:lap0 + snake]) == sorted(plain[lap0:lap0 + snake])
 
 
-def test_snake_pairs_long_and_short_contexts_on_a_cu():
-    # work-groups i and i + snake share a CU when the grid is resident: rank i pairs with the
-    # mirrored rank, so every CU gets one of the longest and one of the shortest contexts
-    lens = list(range(100, 0, -1))  # 100 sequences, already longest first
-    units = [decode_unit(j, lens, 1, 50) for j in range(100)]
-    sums = [lens[units[i][0]] + lens[units[i + 50][0]] for i in range(50)]
-    assert max(sums) == min(sums) == 101
+@pytest.mark.parametrize("seed", range(12))
+def test_packed_decode_rows_rank_first_and_keep_the_snake(seed):
+    # a packed batch: only the 1-token rows take part; the others rank last, and the snake
+    # order holds when the 1-token rows' units fit the resident grid, however many others there are
+    rng = np.random.default_rng(1000 + seed)
+    n = int(rng.integers(2, 60))
+    hkv = int(rng.choice([1, 2, 8]))
+    lens = rng.integers(1, 400, size=n).tolist()
+    q = rng.choice([0, 1, 1, 1, 5, 40], size=n).tolist()
+    active = sum(1 for x in q if x == 1)
+    for snake, resident in ((16, active * hkv), (16, active * hkv - 1), (5, 10 ** 6)):
+        units = [decode_unit(j, lens, hkv, snake, resident, q) for j in range(n * hkv)]
+        assert sorted(units) == [(s, g) for s in range(n) for g in range(hkv)]
+        head = units[:active * hkv]  # the 1-token rows' units come first
+        assert all(q[s] == 1 for s, _ in head) and all(q[s] != 1 for s, _ in units[active * hkv:])
+        plain = sorted(head, key=lambda u: (-lens[u[0]], u[0], u[1]))
+        if resident >= active * hkv:  # snake: each lap of the plain order, odd laps mirrored
+            for lap0 in range(0, active * hkv, snake):
+                lap = plain[lap0:lap0 + snake]
+                want = lap[::-1] if (lap0 // snake) & 1 else lap
+                assert [lens[s] for s, _ in head[lap0:lap0 + snake]] == [lens[s] for s, _ in want]
+        else:  # too many to be resident: plain longest-first order
+            assert [lens[s] for s, _ in head] == [lens[s] for s, _ in plain]
 
 
 # ---------------------------------------------------------------- prefill: rank -> unit
