@@ -62,8 +62,9 @@
  * Conventions for every entry point
  *   - All pointers are device pointers unless stated; the caller owns every buffer.
  *     The library never allocates or frees device memory and never synchronises.  Its
- *     state is a thread-local error string and the host objects a caller creates and
- *     destroys (block managers, schedulers); the attention and cache calls are re-entrant.
+ *     state is a thread-local error string, the host objects a caller creates and
+ *     destroys (block managers, schedulers) and one fixed scratch array per GPU that only
+ *     paged_attention_decode_static uses; the other attention and cache calls are re-entrant.
  *   - Work is enqueued on `stream`; calls return before the device has finished.
  *   - Scalar arguments and pointer alignment are checked on the host before anything
  *     is enqueued: a bad value returns PA_ERR_INVALID_ARGUMENT, a well-formed but
@@ -220,6 +221,29 @@ pa_status_t paged_attention_decode(void* out, const void* query, const void* key
                                    int32_t max_context_len, float scale, pa_dtype_t q_dtype,
                                    pa_dtype_t kv_dtype, int32_t partition_size, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_attention_decode_static -- paged_attention_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks and result as paged_attention_decode, without the workspace:
+ * the split-KV partials go to a scratch array the library holds on every GPU it runs on, until the
+ * process ends (PA_STATIC_WORKSPACE_BYTES per GPU).  A call whose split needs more scratch than
+ * that (paged_attention_workspace_size(...) > PA_STATIC_WORKSPACE_BYTES) returns
+ * PA_ERR_WORKSPACE_TOO_SMALL and launches nothing.  The call allocates and frees nothing.
+ * Every call on one GPU uses that GPU's one array, which keeps the last call's partials (nothing in
+ * it has to start at zero: a call writes every partial it reads): two calls that overlap on one GPU
+ * (on different streams, or from different host threads without ordering) race on it, and the
+ * caller orders them (one stream, or events).
+ */
+#define PA_STATIC_WORKSPACE_BYTES (32u << 20)
+
+pa_status_t paged_attention_decode_static(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                          int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                          int32_t max_context_len, float scale, pa_dtype_t q_dtype,
+                                          pa_dtype_t kv_dtype, int32_t partition_size, hipStream_t stream);
 
 /*
  * The two passes of paged_attention_decode, for callers that schedule or time them

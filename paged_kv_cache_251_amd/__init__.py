@@ -25,6 +25,7 @@ from .binding import (  # noqa: F401
     new_int8_pool,
     paged_attention_decode,
     paged_attention_decode_append,
+    paged_attention_decode_static,
     paged_attention_varlen,
     slot_mapping,
     workspace_size,

@@ -54,6 +54,8 @@ SIGNATURES = {
     "paged_attention_auto_partition": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "paged_attention_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                               _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _i32, _vp, _sz, _vp]),
+    "paged_attention_decode_static": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int, _i32, _vp]),
     "paged_attention_decode_partitions": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                          _i32, _i32, _i32, _i32, _f32, ctypes.c_int, ctypes.c_int,
                                                          _i32, _vp, _sz, _vp]),
@@ -273,6 +275,35 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
         _ptr(context_lens), n, hkv, g, d, bs, nb, max_context_len, scale, dtype_code(query),
         dtype_code(key_cache), partition_size, _ptr(workspace), 0 if workspace is None else workspace.numel(),
         _stream()))
+    return out
+
+
+STATIC_WORKSPACE_BYTES = 32 << 20  # PA_STATIC_WORKSPACE_BYTES
+
+
+def paged_attention_decode_static(query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                                  scale: float, partition_size: int = -1,
+                                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention whose split-KV partials go to the library's own scratch
+    (``paged_attention_decode_static``): no workspace is allocated by the call.  Pass ``out`` to
+    make the whole call allocation-free."""
+    _dev(query, key_cache, value_cache, block_tables, context_lens)
+    _int32(block_tables, context_lens)
+    n, hq, d = query.shape
+    nb, hkv, bs, pd = _pool_dims(key_cache)
+    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
+    _expect(block_tables.dim() == 2 and block_tables.shape[0] == n and context_lens.shape == (n,),
+            "block_tables [N, max_blocks], context_lens [N]")
+    if out is None:
+        out = torch.empty_like(query)
+    _dev(out)
+    _expect(out.shape == query.shape and out.dtype == query.dtype, "out must match query")
+    _check("paged_attention_decode_static", lib().paged_attention_decode_static(
+        _ptr(out), _ptr(query), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), n, hkv, hq // hkv, d, bs, nb, max_context_len, scale, dtype_code(query),
+        dtype_code(key_cache), partition_size, _stream()))
     return out
 
 

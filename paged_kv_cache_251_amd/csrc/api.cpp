@@ -334,6 +334,41 @@ pa_status_t paged_attention_decode(void* out, const void* query, const void* key
   return device_status(e, fn);
 }
 
+static_assert(pa::kStaticWorkspaceBytes == PA_STATIC_WORKSPACE_BYTES, "scratch size of the header and the library");
+
+pa_status_t paged_attention_decode_static(void* out, const void* query, const void* key_cache,
+                                          const void* value_cache, const int32_t* block_tables,
+                                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                          int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                                          int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                                          float scale, pa_dtype_t q_dtype, pa_dtype_t kv_dtype,
+                                          int32_t partition_size, hipStream_t stream) {
+  const char* fn = "paged_attention_decode_static";
+  pa_status_t st = check_attention(fn, num_seqs, num_kv_heads, gqa_group, head_dim, block_size, num_blocks,
+                                   max_blocks_per_seq, max_context_len, scale, q_dtype, kv_dtype, partition_size);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0) return ok();
+  const size_t need = paged_attention_workspace_size(num_seqs, num_kv_heads, gqa_group, head_dim, max_context_len,
+                                                     partition_size);
+  if (need > PA_STATIC_WORKSPACE_BYTES)
+    return fail(PA_ERR_WORKSPACE_TOO_SMALL, "%s: the split needs %zu bytes of scratch, the library holds %zu", fn,
+                need, static_cast<size_t>(PA_STATIC_WORKSPACE_BYTES));
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = pa::static_workspace(&ws);
+    if (e != hipSuccess) return fail(PA_ERR_DEVICE, "%s: scratch address: %s", fn, hipGetErrorString(e));
+  }
+  pa::DecodeParams p;
+  st = prepare_decode(fn, p, out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens,
+                      num_seqs, num_kv_heads, gqa_group, head_dim, block_size, num_blocks, max_context_len, scale,
+                      q_dtype, kv_dtype, partition_size, ws, need > 0 ? PA_STATIC_WORKSPACE_BYTES : 0, true);
+  if (st != PA_OK) return st;
+  hipError_t e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
+  if (e == hipSuccess) e = pa::launch_decode_reduce(p, q_dtype == PA_BF16, head_dim, num_kv_heads * gqa_group,
+                                                    num_seqs, stream);
+  return device_status(e, fn);
+}
+
 pa_status_t paged_attention_decode_partitions(void* out, const void* query, const void* key_cache,
                                               const void* value_cache, const int32_t* block_tables,
                                               int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -27,6 +27,7 @@
 //  * Rows, then waves, are merged at the end; a single partition writes the output,
 //    several write (o/l, m, l) to the workspace for the reduce kernel.
 #include <atomic>
+#include <mutex>
 
 #include "pa_device.hpp"
 #include "pa_launch.hpp"
@@ -840,6 +841,34 @@ hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_d
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Split-KV scratch of the entry point that allocates nothing: one array per GPU, held until the
+// process ends.  In host code `scratch` is only a stand-in for the symbol, not a device address;
+// the address of the current device's copy comes from hipGetSymbolAddress, taken once per device
+// (with that device current) and kept.  The partition pass writes every partial the reduce pass
+// reads in the same call, so nothing in it has to start at zero.
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+hipError_t static_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace pa

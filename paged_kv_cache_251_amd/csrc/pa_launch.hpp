@@ -58,6 +58,12 @@ struct DecodeParams {
 // (o/l, m, l) per partition in the workspace.
 hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
                                     hipStream_t stream);
+// Bytes of the split-KV scratch array the library holds on every GPU (the decode entry point
+// that allocates nothing); equals PA_STATIC_WORKSPACE_BYTES of the public header.
+constexpr size_t kStaticWorkspaceBytes = size_t(32) << 20;
+// Device address of that array on the current device (looked up once per device).
+hipError_t static_workspace(void** ptr);
+
 // Merge pass over the split sequences (no-op when p.max_parts <= 1).
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
                                 hipStream_t stream);

@@ -152,3 +152,27 @@ def test_workspace_size_and_auto_partition(lib):
     p = lib.paged_attention_auto_partition(64, 8, 4, 128, 2048)
     assert p == 0 or (p % 256 == 0 and p < 2048)
     assert ws(64, 8, 4, 128, 2048, -1) == ws(64, 8, 4, 128, 2048, p)
+
+
+def _decode_static(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mb=1024, lens=FAKE, n=4, hkv=8, g=4, d=128, bs=16, nb=8,
+             maxl=64, scale=0.1, qd=1, kd=1, part=0)
+    a.update(kw)
+    return lib.paged_attention_decode_static(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mb"], a["lens"], a["n"],
+                                             a["hkv"], a["g"], a["d"], a["bs"], a["nb"], a["maxl"], a["scale"],
+                                             a["qd"], a["kd"], a["part"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    # 4 sequences x 32 heads x 1024 partitions of 16 tokens: 68 MB of partials > the 32 MiB scratch
+    (dict(maxl=16384, part=16), 3),
+    (dict(n=-1), 1), (dict(g=3), 2), (dict(part=100), 1), (dict(out=None), 1), (dict(q=FAKE + 4), 1),
+    (dict(qd=0, kd=1), 2),
+])
+def test_decode_static_rejects_on_host(lib, kw, status):
+    """The allocation-free decode checks its arguments like paged_attention_decode and refuses a
+    split whose partials do not fit the library's scratch array, before any device call."""
+    assert _decode_static(lib, **kw) == status
+    assert lib.pa_last_error().decode()
+    if status == 3:
+        assert "scratch" in lib.pa_last_error().decode()
