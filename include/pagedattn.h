@@ -180,7 +180,10 @@ size_t paged_attention_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                       int32_t gqa_group, int32_t head_dim,
                                       int32_t max_context_len, int32_t partition_size);
 
-/* The partition size (tokens) that partition_size = -1 resolves to. */
+/* The partition size (tokens) that partition_size = -1 resolves to on the current device: 0 (one
+ * pass per context) when the (sequence, KV head) contexts are at least the device's CU count,
+ * otherwise a multiple of 256 tokens aiming at about 8 work-groups per CU (256 CUs are assumed
+ * when no device can be queried). */
 int32_t paged_attention_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t gqa_group, int32_t head_dim,
                                        int32_t max_context_len);
@@ -212,6 +215,12 @@ int32_t paged_attention_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
  *   workspace     device buffer of at least paged_attention_workspace_size(...) bytes
  *                 (may be NULL when that size is 0), 256-byte aligned; its contents
  *                 are scratch, overwritten on every call
+ * Query range over 8-bit caches: with an FP8_E5M2, INT8 or FP8_E4M3 cache the bf16 query is
+ * taken to f16 for the dot products.  That is exact for elements of magnitude 2^-14 .. 65280
+ * (every bf16 value f16 can hold); smaller elements keep f16's subnormal precision.  Queries must
+ * stay below 65536 in magnitude on these caches: a larger element overflows to inf, and the output
+ * row of its (sequence, head) is then unspecified (zero or not finite, by path); every other head
+ * and sequence is unaffected.
  */
 pa_status_t paged_attention_decode(void* out, const void* query, const void* key_cache,
                                    const void* value_cache, const int32_t* block_tables,
@@ -328,7 +337,9 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
  * max_q_len >= 2 no sequence has a single row and the decode kernel is not launched; when
  * max_q_len <= 1 only the decode kernel is.
  * Supported: bf16 query; bf16 or FP8_E5M2 cache (E5M2 codes widen exactly to f16, and the
- * multi-token rows then run on the f16 MFMA with the query and the probabilities in f16).  A row
+ * multi-token rows then run on the f16 MFMA with the query and the probabilities in f16; the
+ * query range is then that of paged_attention_decode over 8-bit caches: below 65536 in
+ * magnitude, a larger element leaving its own row and head unspecified).  A row
  * whose position is negative (n_s > L) sees no key and comes out zero.
  */
 pa_status_t paged_attention_varlen(void* out, const void* query, const void* key_cache, const void* value_cache,

@@ -14,7 +14,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# PA_LIBRARY names another build of the same library (the host-sanitized one)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_F32, PA_BF16, PA_FP8_E5M2, PA_INT8, PA_FP8_E4M3 = 0, 1, 2, 3, 4
 INT8_BLOCK = 16  # tokens per block of a scaled (INT8 / FP8_E4M3) pool

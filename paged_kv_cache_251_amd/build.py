@@ -1,6 +1,13 @@
 """Build libpagedattn.so in-tree with hipcc for gfx950.
 
-    python -m paged_kv_cache_251_amd.build
+    python -m paged_kv_cache_251_amd.build              # libpagedattn.so
+    python -m paged_kv_cache_251_amd.build --sanitize   # libpagedattn_san.so
+
+The sanitized library has its host code (the C ABI, the block manager, the scheduler) built with
+AddressSanitizer and UndefinedBehaviorSanitizer (host side only; the kernels are built as usual).
+It is loaded in place of the plain one with PA_LIBRARY=<path> and the sanitizer runtime preloaded
+(sanitizer_env() gives the environment); tests/test_sanitize_cpu.py runs the host-side tests that
+way.
 """
 from __future__ import annotations
 
@@ -16,8 +23,15 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
+OBJ_SAN = os.path.join(PKG, "_build_san")
+LIB_SAN = os.path.join(PKG, "libpagedattn_san.so")
+HOST_SOURCES = ("api.cpp", "block_manager.cpp", "scheduler.cpp")
+# host-side sanitizers; every -fsanitize flag applies to the host compilation only
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
 
-SOURCES = ["api.cpp", "block_manager.cpp", "scheduler.cpp", "cache_write.hip", "decode.hip", "varlen.hip", "multiquery.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "scheduler.cpp", "cache_write.hip", "decode.hip", "varlen.hip", "multiquery.hip", "packed.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -42,9 +56,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
+    out = os.path.join(OBJ_SAN if sanitize else OBJ, os.path.splitext(src)[0] + ".o")
+    extra = SANITIZE if sanitize and src in HOST_SOURCES else []
+    cmd = [_hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,18 +71,45 @@ def _compile(src: str, verbose: bool) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    os.makedirs(OBJ_SAN if sanitize else OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), SOURCES))
+    lib = LIB_SAN if sanitize else LIB
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """The compiler's shared AddressSanitizer runtime (it carries the UndefinedBehaviorSanitizer
+    handlers too)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    import glob
+
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/*/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+    return found[-1]
+
+
+def sanitizer_env(base=None) -> dict:
+    """Environment for a host-only process that loads the sanitized library through the binding."""
+    env = dict(os.environ if base is None else base)
+    env["PA_LIBRARY"] = LIB_SAN
+    env["LD_PRELOAD"] = sanitizer_runtime()
+    # the interpreter itself is not instrumented: its own allocations are not leak-checked
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=1:halt_on_error=1"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1"
+    return env
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

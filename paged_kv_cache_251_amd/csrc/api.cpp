@@ -70,6 +70,10 @@ constexpr int64_t kMaxGridYZ = 65535;
 #endif
 constexpr size_t kWsAlign = 256;
 
+#ifndef PA_PACKED_ONE_LAUNCH
+#define PA_PACKED_ONE_LAUNCH 1  // a packed step with prefill chunks and decode tokens: one two-role launch
+#endif
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Partition count of the longest context, or 1 when unsplit.
@@ -95,12 +99,15 @@ WsLayout ws_layout(int64_t rows, int64_t hkv, int64_t gqa, int64_t head_dim, int
 }
 
 int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  // With at least one (KV head, sequence) context per CU (256 CUs) every context is
-  // streamed whole, longest first: no partial results, no merge.  Fewer, longer contexts
-  // are split into multiples of 256 tokens, aiming at ~2048 work-groups.
+  // With at least one (KV head, sequence) context per CU of the current device every context is
+  // streamed whole, longest first: no partial results, no merge.  Fewer, longer contexts are
+  // split into multiples of 256 tokens, aiming at ~8 work-groups per CU.  Without a device to
+  // ask (a host-only process), the MI355X's 256 CUs are assumed.
+  const int cus_queried = pa::current_device_cus();
+  const int64_t cus = cus_queried > 0 ? cus_queried : 256;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  if (units <= 0 || units >= 256 || max_context_len <= 256) return 0;
-  int64_t p = static_cast<int64_t>(max_context_len) * units / 2048;
+  if (units <= 0 || units >= cus || max_context_len <= 256) return 0;
+  int64_t p = static_cast<int64_t>(max_context_len) * units / (8 * cus);
   p = (p + 255) / 256 * 256;
   if (p < 256) p = 256;
   if (p >= max_context_len) return 0;
@@ -466,6 +473,13 @@ pa_status_t paged_attention_varlen(void* out, const void* query, const void* key
   // num_seqs * max_q_len >= 2 * num_seqs none has a single row: no decode launch.
   const bool single_rows = !(max_q_len >= 2 && static_cast<int64_t>(total_q) == static_cast<int64_t>(num_seqs) * max_q_len);
   hipError_t e = hipSuccess;
+  const bool prefill_rows = max_q_len >= 2 && !pa::multiquery_applies(gqa_group, max_q_len);
+  if (PA_PACKED_ONE_LAUNCH && single_rows && prefill_rows && pa::packed_step_applies(p, num_seqs, max_q_len)) {
+    // decode tokens and prefill chunks together: one two-role launch
+    return device_status(pa::launch_packed_step(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, total_q,
+                                                max_q_len, stream),
+                         fn);
+  }
   if (single_rows) {
     e = pa::launch_decode_partitions(p, kv_kind(kv_dtype), head_dim, gqa_group, num_seqs, stream);
     if (e == hipSuccess) e = pa::launch_decode_reduce(p, true, head_dim, num_kv_heads * gqa_group, num_seqs, stream);

@@ -58,6 +58,9 @@ struct DecodeParams {
 // (o/l, m, l) per partition in the workspace.
 hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
                                     hipStream_t stream);
+// Compute units of the current device (0 when it cannot be queried).
+int current_device_cus();
+
 // Bytes of the split-KV scratch array the library holds on every GPU (the decode entry point
 // that allocates nothing); equals PA_STATIC_WORKSPACE_BYTES of the public header.
 constexpr size_t kStaticWorkspaceBytes = size_t(32) << 20;
@@ -77,6 +80,12 @@ hipError_t launch_varlen_multiquery(const DecodeParams& p, int kv_kind, int head
 // Prefill rows (sequences with >= 2 query tokens) of a packed batch, on MFMA (bf16 or E5M2 cache).
 hipError_t launch_varlen_prefill(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs, int total_q,
                                  int max_q_len, hipStream_t stream);
+
+// A packed step with both prefill chunks and decode tokens as one two-role launch (whole-context
+// decode passes only, at most 1024 sequences).
+bool packed_step_applies(const DecodeParams& p, int num_seqs, int max_q_len);
+hipError_t launch_packed_step(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs, int total_q,
+                              int max_q_len, hipStream_t stream);
 
 hipError_t launch_slot_mapping(int32_t* slots, const int32_t* cu, const int32_t* end_pos,
                                const int32_t* tables, int32_t max_blocks, int32_t num_seqs,

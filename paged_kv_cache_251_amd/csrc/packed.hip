@@ -1,0 +1,105 @@
+// One launch for a packed (varlen) step that holds both prefill chunks and decode tokens.
+//
+// The release post's continuous batching (Colossal-Inference, "连续批量化算法 (Continuous
+// Batching)") keeps prefill and decode tokens in one unpadded 1-D batch; the optimisation
+// overview (2.3.2 "高性能算子") notes that prefill is GEMM-bound and decode GEMV-bound, so the two
+// use different parts of the chip: the matrix cores, and the memory system.  Run back to back,
+// each leaves the other's part idle.  Here one grid carries both roles: work-group i is either a
+// prefill unit (a 128-row query tile of one KV head, on MFMA; prefill_body.hpp) or a decode unit
+// (one (sequence, KV head) context streamed whole; decode_body.hpp), the roles interleaved evenly
+// in dispatch order, each list longest first.  A CU then holds work-groups of both roles at once:
+// while one waits on HBM the other keeps the matrix cores busy.
+//
+// The decode role runs only whole-context passes (no split-KV partitions; the caller's launch
+// falls back to the two kernels otherwise).
+#include "decode_body.hpp"
+#include "pa_device.hpp"
+#include "pa_launch.hpp"
+#include "prefill_body.hpp"
+
+namespace pa {
+
+// LDS of a two-role work-group: the larger of the two roles' needs.
+template <int D, int G>
+struct PackedSmem {
+  static constexpr int DEC = DecodeSmem<G, D, 4>::BYTES;
+  static constexpr int PRE = PrefillSmem<D>::BYTES;
+  static constexpr int BYTES = DEC > PRE ? DEC : PRE;
+};
+
+// Position i of the dispatch order holds a prefill work-group when floor((i+1) n_pre / total) >
+// floor(i n_pre / total): the n_pre prefill work-groups are spread evenly over the total.
+__device__ __forceinline__ int2 packed_role(int i, int n_pre, int total) {
+  const long long before = (long long)i * n_pre / total;
+  const long long upto = (long long)(i + 1) * n_pre / total;
+  return upto > before ? make_int2(1, (int)before) : make_int2(0, i - (int)before);
+}
+
+template <int D, int G, bool E8>
+__global__ __launch_bounds__(256, 2) void packed_step_kernel(const DecodeParams p, int n_pre, int n_dec) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PackedSmem<D, G>::BYTES];
+  const int2 r = packed_role(blockIdx.x, n_pre, n_pre + n_dec);
+  if (r.x) {
+    prefill_body<D, G, E8>(p, r.y, 0, 0, 1, reinterpret_cast<uint16_t*>(smem));
+  } else {
+    constexpr int KV = E8 ? KV_E5M2 : KV_BF16;
+    int* sm_i = reinterpret_cast<int*>(smem);
+    float* sm_f = reinterpret_cast<float*>(smem + 4 * DecodeSmem<G, D, 4>::INTS);
+    decode_body<KV, D, G, 4>(p, r.y % p.num_kv_heads, 0, r.y / p.num_kv_heads, p.num_kv_heads, n_dec / p.num_kv_heads,
+                             sm_i, sm_f);
+  }
+}
+
+template <int D, int G, bool E8>
+static hipError_t launch_packed_dg(const DecodeParams& p, int num_seqs, int total_q, int max_q_len,
+                                   hipStream_t stream) {
+  constexpr int TOKW = 128 / G;
+  DecodeParams q = p;
+  // prefill work-groups: as many as the longest-first schedule can hand units to (see the
+  // prefill kernel's launcher); the spare ones return at once
+  const long long tiles_per_seq = (max_q_len + TOKW - 1) / TOKW;
+  const long long chunks = std::min<long long>(num_seqs, total_q / 2);
+  const long long units = std::min<long long>((total_q + chunks * (TOKW - 1)) / TOKW, tiles_per_seq * num_seqs);
+  const long long n_pre = units * p.num_kv_heads;
+  const long long n_dec = (long long)num_seqs * p.num_kv_heads;
+  if (n_pre + n_dec > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  q.sched_seqs = num_seqs;
+  q.longest_first = 1;
+  q.snake = 0;
+  q.resident = 0;
+  hipLaunchKernelGGL((packed_step_kernel<D, G, E8>), dim3((unsigned)(n_pre + n_dec)), dim3(256), 0, stream, q,
+                     (int)n_pre, (int)n_dec);
+  return hipGetLastError();
+}
+
+template <int D, bool E8>
+static hipError_t launch_packed_d(const DecodeParams& p, int gqa, int num_seqs, int total_q, int max_q_len,
+                                  hipStream_t stream) {
+  switch (gqa) {
+    case 1: return launch_packed_dg<D, 1, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 2: return launch_packed_dg<D, 2, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 4: return launch_packed_dg<D, 4, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 8: return launch_packed_dg<D, 8, E8>(p, num_seqs, total_q, max_q_len, stream);
+    case 16: return launch_packed_dg<D, 16, E8>(p, num_seqs, total_q, max_q_len, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool packed_step_applies(const DecodeParams& p, int num_seqs, int max_q_len) {
+  return p.max_parts <= 1 && num_seqs <= kMaxScheduledSeqs && num_seqs <= kMaxRankedSeqs && max_q_len >= 2;
+}
+
+hipError_t launch_packed_step(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs, int total_q,
+                              int max_q_len, hipStream_t stream) {
+  const bool e8 = kv_kind == KV_E5M2;
+  if (!e8 && kv_kind != KV_BF16) return hipErrorInvalidValue;
+  if (head_dim == 128)
+    return e8 ? launch_packed_d<128, true>(p, gqa, num_seqs, total_q, max_q_len, stream)
+              : launch_packed_d<128, false>(p, gqa, num_seqs, total_q, max_q_len, stream);
+  if (head_dim == 64)
+    return e8 ? launch_packed_d<64, true>(p, gqa, num_seqs, total_q, max_q_len, stream)
+              : launch_packed_d<64, false>(p, gqa, num_seqs, total_q, max_q_len, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

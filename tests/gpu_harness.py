@@ -106,9 +106,9 @@ class DeviceBatch:
             self.write(ph, seqs)
         self.q = to_device(queries(w), w.q_dtype)
 
-    def write(self, phase: str, seqs=None):
+    def write(self, phase: str, seqs=None, plan=None):
         w = self.w
-        plan = write_plan(w, phase, seqs)
+        plan = write_plan(w, phase, seqs) if plan is None else plan
         cu = torch.from_numpy(plan.cu).to(DEV)
         end = torch.from_numpy(plan.end_pos).to(DEV)
         slots = pa.slot_mapping(cu, end, self.tables, plan.num_tokens, w.num_blocks, w.block_size)
@@ -122,6 +122,35 @@ class DeviceBatch:
         w = self.w
         return pa.paged_attention_decode(self.q, self.pk, self.pv, self.tables, self.lens, w.max_context_len,
                                          w.scale, partition_size=partition_size, out=out)
+
+
+_E5M2_OF_BF16 = []
+
+
+def e5m2_of_bf16() -> np.ndarray:
+    """The oracle's own E5M2 encoder evaluated once on all 65,536 bf16 bit patterns (indexed by
+    the pattern), so that a full-size pool is encoded by lookup instead of element by element."""
+    if not _E5M2_OF_BF16:
+        bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+        _E5M2_OF_BF16.append(oracle.f64_to_e5m2(oracle.bf16_to_f64(bits)))
+    return _E5M2_OF_BF16[0]
+
+
+def oracle_pools_from_plan(w, plan):
+    """Oracle pools of one write plan, as oracle.cache_write fills them; a bf16 -> E5M2 write
+    takes each row's codes from the tabulated oracle encoder (the same bytes: a pure function of
+    the bf16 pattern)."""
+    pk = oracle.new_pool(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.kv_dtype, POISON_BITS[w.kv_dtype])
+    pv = pk.copy()
+    slots = oracle.slot_mapping(w.block_tables, plan.counts, plan.end_pos, w.block_size).astype(np.int64)
+    keep = slots >= 0
+    blk, off = slots[keep] // w.block_size, slots[keep] % w.block_size
+    for pool, rows in ((pk, plan.k), (pv, plan.v)):
+        if w.src_dtype == "bf16" and w.kv_dtype == "e5m2":
+            pool[blk, off] = e5m2_of_bf16()[np.asarray(rows, np.uint16)[keep]]
+        else:
+            oracle.cache_write(pool, rows, slots, w.src_dtype, w.kv_dtype, w.block_size)
+    return pk, pv
 
 
 def oracle_pools(w, phases=("all",), seqs=None):

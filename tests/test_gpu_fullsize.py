@@ -1,11 +1,11 @@
-"""Full-size parity on sampled sequences (needs an MI355X).
+"""Full-size parity of every sequence (needs an MI355X).
 
 The Llama-3-8B E5M2 decode workload (128 sequences up to 4096 tokens) and the long-context
 split-KV workload (8 x 32768 tokens, 512-token partitions) are written and attended on the
-GPU at their real sizes, in the launch configurations bench.py times; the oracle checks a
-sample of sequences one by one (its pool holds only the sampled sequences' blocks).
-The split-KV partials left in the workspace are checked against the oracle's per-partition
-softmax state, independently of the reduce kernel.
+GPU at their real sizes, in the launch configurations bench.py times, and every output row is
+compared with the float64 oracle run on the same pools.  The whole E5M2 pools are compared byte
+for byte with the oracle's cast.  The split-KV partials left in the workspace are checked against
+the oracle's per-partition softmax state, independently of the reduce kernel.
 """
 import numpy as np
 import pytest
@@ -13,51 +13,45 @@ import torch
 
 import oracle
 import paged_kv_cache_251_amd as pa
-from gpu_harness import DEV, DeviceBatch, assert_close, canonical, oracle_pools, out_f64
-from workloads import make_config, make_workload, queries
+from gpu_harness import DEV, DeviceBatch, assert_close, canonical, oracle_pools, oracle_pools_from_plan, out_f64
+from workloads import make_config, make_workload, queries, write_plan
 
 pytestmark = pytest.mark.gpu
 
 
-def _sample(w, k, seed):
-    rng = np.random.default_rng(seed)
-    # always include the longest and the shortest context
-    order = np.argsort(w.context_lens)
-    pick = set([int(order[0]), int(order[-1])]) | set(rng.choice(w.num_seqs, size=k, replace=False).tolist())
-    return sorted(pick)
+def _full_batch(w):
+    """The workload written on the GPU by the library and on the CPU by the oracle, from one plan."""
+    plan = write_plan(w, "all")
+    b = DeviceBatch(w, phases=())
+    b.write("all", plan=plan)
+    pk, pv = oracle_pools_from_plan(w, plan)
+    return b, pk, pv
 
 
-def test_e5m2_decode_full_size_sampled():
+def test_e5m2_decode_full_size_every_sequence():
     w = make_config(3)
-    b = DeviceBatch(w)
-    sel = _sample(w, 6, 31)
-    pk, pv = oracle_pools(w, seqs=sel)
-    # cache bytes of every sampled sequence's blocks: bit-exact E5M2 cast
-    gk, gv = canonical(b.pk, "e5m2"), canonical(b.pv, "e5m2")
-    for s in sel:
-        L = int(w.context_lens[s])
-        assert np.array_equal(oracle.gather_kv(gk, w.block_tables[s], L, 16), oracle.gather_kv(pk, w.block_tables[s], L, 16))
-        assert np.array_equal(oracle.gather_kv(gv, w.block_tables[s], L, 16), oracle.gather_kv(pv, w.block_tables[s], L, 16))
-    ref = oracle.paged_decode(pk, pv, "e5m2", queries(w), "bf16", w.block_tables, w.context_lens, 16, w.scale, seqs=sel)
+    b, pk, pv = _full_batch(w)
+    # the whole pools, written slots and poisoned spares alike: bit-exact E5M2 cast
+    assert np.array_equal(canonical(b.pk, "e5m2"), pk)
+    assert np.array_equal(canonical(b.pv, "e5m2"), pv)
+    ref = oracle.paged_decode(pk, pv, "e5m2", queries(w), "bf16", w.block_tables, w.context_lens, 16, w.scale)
     for part in (-1, 512):
-        out = out_f64(b.decode(part), "bf16")[sel]
+        out = out_f64(b.decode(part), "bf16")
         err = assert_close(out, ref, "bf16", f"e5m2 full size partition {part}")
-        print(f"e5m2 full size partition {part}: max abs err {err:.2e}")
+        print(f"e5m2 full size, all {w.num_seqs} sequences, partition {part}: max abs err {err:.2e}")
 
 
-def test_long_context_split_kv_full_size_sampled():
+def test_long_context_split_kv_full_size_every_sequence():
     w = make_config(4)
-    b = DeviceBatch(w)
-    sel = [0, 5]
-    pk, pv = oracle_pools(w, seqs=sel)
-    ref = oracle.paged_decode(pk, pv, "bf16", queries(w), "bf16", w.block_tables, w.context_lens, 16, w.scale, seqs=sel)
+    b, pk, pv = _full_batch(w)
+    ref = oracle.paged_decode(pk, pv, "bf16", queries(w), "bf16", w.block_tables, w.context_lens, 16, w.scale)
     part = w.partition_size
     need = pa.workspace_size(w.num_seqs, w.num_kv_heads, w.gqa_group, w.head_dim, w.max_context_len, part)
     ws = pa.alloc_workspace(need, DEV)
     out = pa.paged_attention_decode(b.q, b.pk, b.pv, b.tables, b.lens, w.max_context_len, w.scale,
                                     partition_size=part, workspace=ws)
-    err = assert_close(out_f64(out, "bf16")[sel], ref, "bf16", "long context split-KV")
-    print(f"long context: max abs err {err:.2e}")
+    err = assert_close(out_f64(out, "bf16"), ref, "bf16", "long context split-KV")
+    print(f"long context, all {w.num_seqs} sequences: max abs err {err:.2e}")
     # the partials: o [N][Hq][P][D], m [N][Hq][P], l [N][Hq][P], each region 256-byte aligned
     n, hq, d = w.num_seqs, w.num_q_heads, w.head_dim
     P = -(-w.max_context_len // part)
@@ -68,18 +62,18 @@ def test_long_context_split_kv_full_size_sampled():
     m = wsf[ob : ob + mb].view(torch.float32)[: n * hq * P].view(n, hq, P).cpu().numpy().astype(np.float64)
     l = wsf[ob + mb : ob + 2 * mb].view(torch.float32)[: n * hq * P].view(n, hq, P).cpu().numpy().astype(np.float64)
     qd = oracle.decode_storage(queries(w), "bf16")
-    s = sel[0]
-    L = int(w.context_lens[s])
-    kk = oracle.decode_storage(oracle.gather_kv(pk, w.block_tables[s], L, 16), "bf16")
-    vv = oracle.decode_storage(oracle.gather_kv(pv, w.block_tables[s], L, 16), "bf16")
-    om, ol, oo = oracle.attend_partitioned(qd[s : s + 1], kk, vv, w.scale, part)
-    # The kernel keeps its running max in base 2 and rescales only when the max grows by more
-    # than a fixed threshold, so the stored m may lag the true maximum; what is fixed is the
-    # log-sum-exp m + log2(l) and the normalised o.
-    lse_ref = (om[:, 0, :].T + np.log(ol[:, 0, :].T)) * np.log2(np.e)
-    np.testing.assert_allclose(m[s] + np.log2(l[s]), lse_ref, rtol=0, atol=1e-4)
-    assert np.all(m[s] <= om[:, 0, :].T * np.log2(np.e) + 1e-4)
-    assert np.abs(o[s] - oo[:, 0].transpose(1, 0, 2)).max() <= 1e-4
+    for s in range(n):
+        L = int(w.context_lens[s])
+        kk = oracle.decode_storage(oracle.gather_kv(pk, w.block_tables[s], L, 16), "bf16")
+        vv = oracle.decode_storage(oracle.gather_kv(pv, w.block_tables[s], L, 16), "bf16")
+        om, ol, oo = oracle.attend_partitioned(qd[s : s + 1], kk, vv, w.scale, part)
+        # The kernel keeps its running max in base 2 and rescales only when the max grows by more
+        # than a fixed threshold, so the stored m may lag the true maximum; what is fixed is the
+        # log-sum-exp m + log2(l) and the normalised o.
+        lse_ref = (om[:, 0, :].T + np.log(ol[:, 0, :].T)) * np.log2(np.e)
+        np.testing.assert_allclose(m[s] + np.log2(l[s]), lse_ref, rtol=0, atol=1e-4)
+        assert np.all(m[s] <= om[:, 0, :].T * np.log2(np.e) + 1e-4)
+        assert np.abs(o[s] - oo[:, 0].transpose(1, 0, 2)).max() <= 1e-4, f"sequence {s} partials"
 
 
 def test_context_of_128k_tokens():

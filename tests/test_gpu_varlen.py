@@ -132,3 +132,25 @@ def test_shared_prefix_equals_private_copy():
     private_out = pa.paged_attention_varlen(b.q, pk, pv, torch.from_numpy(w.cu_seqlens_q).to(DEV), b.lens, tables,
                                             w.max_q_len, w.max_context_len, w.scale, partition_size=0)
     assert torch.equal(shared_out.view(torch.int16), private_out.view(torch.int16))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e5m2"])
+def test_one_launch_equals_the_rows_called_apart(kv):
+    """A packed step with both prefill chunks and decode tokens runs as one two-role launch; its
+    output equals, bit for bit, the prefill chunks and the decode tokens each called on their own
+    (the decode tokens then run on the plain decode kernel)."""
+    w = dataclasses.replace(make_config(5), src_dtype="bf16", kv_dtype=kv)
+    b = DeviceBatch(w)
+    full = _varlen(b, 0)
+    n_pre = int((w.q_lens > 1).sum())
+    assert np.all(w.q_lens[:n_pre] > 1) and np.all(w.q_lens[n_pre:] == 1)  # chunks packed first
+    rows = int(w.cu_seqlens_q[n_pre])
+    cu = torch.from_numpy(w.cu_seqlens_q).to(DEV)
+    pre = pa.paged_attention_varlen(b.q[:rows].contiguous(), b.pk, b.pv, cu[: n_pre + 1].contiguous(), b.lens[:n_pre],
+                                    b.tables[:n_pre].contiguous(), w.max_q_len, w.max_context_len, w.scale,
+                                    partition_size=0)
+    dec = pa.paged_attention_varlen(b.q[rows:].contiguous(), b.pk, b.pv, (cu[n_pre:] - rows).contiguous(),
+                                    b.lens[n_pre:].contiguous(), b.tables[n_pre:].contiguous(), 1, w.max_context_len,
+                                    w.scale, partition_size=0)
+    assert torch.equal(full[:rows].view(torch.int16), pre.view(torch.int16))
+    assert torch.equal(full[rows:].view(torch.int16), dec.view(torch.int16))
