@@ -35,9 +35,34 @@ __device__ __forceinline__ int2 packed_role(int i, int n_pre, int total) {
   return upto > before ? make_int2(1, (int)before) : make_int2(0, i - (int)before);
 }
 
+// Prefill work-groups the batch really needs: ceil(n_s / TOKW) query tiles of every sequence with
+// n_s >= 2 rows, per KV head (the host only knows an upper bound).  Wave 0 counts, every wave reads.
+template <int TOKW>
+__device__ __forceinline__ int packed_prefill_units(const DecodeParams& p, int num_seqs, int* sm) {
+  if (threadIdx.x < 64) {
+    int c = 0;
+    for (int s = threadIdx.x; s < num_seqs; s += 64) {
+      const int n = load_invariant(p.cu_q + s + 1) - load_invariant(p.cu_q + s);
+      c += n >= 2 ? (n + TOKW - 1) / TOKW : 0;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+    if (threadIdx.x == 0) *sm = c * p.num_kv_heads;
+  }
+  __syncthreads();
+  const int u = *sm;
+  __syncthreads();  // the slot is reused by the roles' own LDS
+  return u;
+}
+
 template <int D, int G, bool E8>
-__global__ __launch_bounds__(256, 2) void packed_step_kernel(const DecodeParams p, int n_pre, int n_dec) {
+__global__ __launch_bounds__(256, 2) void packed_step_kernel(const DecodeParams p, int n_pre_bound, int n_dec) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PackedSmem<D, G>::BYTES];
+  // The roles are interleaved over the prefill work-groups the batch needs, not the host's bound;
+  // the grid's surplus (the bound minus that count) sits at the end and returns at once.
+  const int n_pre =
+      min(n_pre_bound, packed_prefill_units<128 / G>(p, n_dec / p.num_kv_heads, reinterpret_cast<int*>(smem)));
+  if ((int)blockIdx.x >= n_pre + n_dec) return;
   const int2 r = packed_role(blockIdx.x, n_pre, n_pre + n_dec);
   if (r.x) {
     prefill_body<D, G, E8>(p, r.y, 0, 0, 1, reinterpret_cast<uint16_t*>(smem));
@@ -45,8 +70,8 @@ __global__ __launch_bounds__(256, 2) void packed_step_kernel(const DecodeParams 
     constexpr int KV = E8 ? KV_E5M2 : KV_BF16;
     int* sm_i = reinterpret_cast<int*>(smem);
     float* sm_f = reinterpret_cast<float*>(smem + 4 * DecodeSmem<G, D, 4>::INTS);
-    decode_body<KV, D, G, 4>(p, r.y % p.num_kv_heads, 0, r.y / p.num_kv_heads, p.num_kv_heads, n_dec / p.num_kv_heads,
-                             sm_i, sm_f);
+    decode_body<KV, D, G, 4>(p, r.y % p.num_kv_heads, 0, r.y / p.num_kv_heads, p.num_kv_heads,
+                             n_dec / p.num_kv_heads, sm_i, sm_f);
   }
 }
 

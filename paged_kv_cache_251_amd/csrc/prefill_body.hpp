@@ -370,7 +370,10 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
       if (ntiles > 2) tb_next = read_table(2);
     }
   }
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // One tile step; MASKED = false for the tiles that every row of the work-group sees whole (no
+  // key past any row's visible range), so their code holds no masking at all.
+  auto tile_step = [&](int kt, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     if (kt + 1 < ntiles) {
       store((kt + 1) & 1);
       if (kt + 2 < ntiles) {
@@ -399,7 +402,7 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
 
     // ---- mask, online softmax (threshold rescale), P in the B-operand key order -----------
     // Masking is needed only where a row's visible range ends inside the tile.
-    const bool whole = __builtin_amdgcn_readfirstlane(kt * KT + KT <= wave_lim_min ? 1 : 0) != 0;
+    const bool whole = !MASKED || __builtin_amdgcn_readfirstlane(kt * KT + KT <= wave_lim_min ? 1 : 0) != 0;
     uint4 pb[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -420,6 +423,7 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
       // The row's running max only moves when some score exceeds it by more than the
       // threshold; the lanes' own maxima decide whether the row maxima are needed at all.
       if (__any(mx * p.scale_log2 > m_run[j] + kTauPrefill)) {  // scale > 0
+        asm volatile("");  // a real branch: the rescale is rare, so it is not executed speculatively
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         mx *= p.scale_log2;
@@ -463,7 +467,13 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
       }
     }
     lds_barrier();
-  }
+  };
+  // tiles below the smallest visible range of the work-group's rows (its first token's) are whole
+  const int wg_lim_min = causal ? min(L, L - n + i0 + 1) : L;
+  const int kt_whole = __builtin_amdgcn_readfirstlane(min(ntiles, max(0, wg_lim_min) / KT));
+  int kt = 0;
+  for (; kt < kt_whole; ++kt) tile_step(kt, std::false_type{});
+  for (; kt < ntiles; ++kt) tile_step(kt, std::true_type{});
 
   // ---- normalise and store: lane l holds dims dt*16 + 4*lg .. +3 of row l%16 --------------
 #pragma unroll
