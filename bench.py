@@ -104,19 +104,21 @@ class Batch:
         self.w = w
         self.tables = torch.from_numpy(w.block_tables).to(dev)
         self.lens = torch.from_numpy(w.context_lens).to(dev)
-        if w.kv_dtype in SCALED:  # codes, then 16 float32 scales per (block, head); every word NaN
-            words = (w.num_blocks, w.num_kv_heads, (w.block_size * w.head_dim + 64) // 4)
+        if w.kv_dtype in SCALED:  # key pool: codes, key scales, value scales; value pool: codes; every word NaN
+            kwords = (w.num_blocks, w.num_kv_heads, (w.block_size * w.head_dim + 128) // 4)
+            vwords = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim // 4)
             store = torch.int8 if w.kv_dtype == "int8" else torch.float8_e4m3fn
-            self.pk = torch.full(words, POISON_BITS[w.kv_dtype], dtype=torch.int32, device=dev).view(store)
+            self.pk = torch.full(kwords, POISON_BITS[w.kv_dtype], dtype=torch.int32, device=dev).view(store)
+            self.pv = torch.full(vwords, POISON_BITS[w.kv_dtype], dtype=torch.int32, device=dev).view(store)
         else:
             shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
             ints = {"f32": torch.int32, "bf16": torch.int16, "e5m2": torch.uint8}[w.kv_dtype]
             store = {"f32": torch.float32, "bf16": torch.bfloat16, "e5m2": torch.uint8}[w.kv_dtype]
             self.pk = torch.full(shape, POISON_BITS[w.kv_dtype], dtype=ints, device=dev).view(store)
-        # every pool kind but INT8 takes the fused append (an E4M3 pool's new row is quantised in the
-        # kernel); an INT8 pool is written by the cache write's quantiser
-        self.fused = w.kv_dtype != "int8"
-        self.pv = self.pk.clone()
+            self.pv = self.pk.clone()
+        # every pool kind takes the fused append (an INT8 or E4M3 pool's new row is quantised in the
+        # kernel with the cache write's rule)
+        self.fused = True
         hist = write_plan(w, "cached")
         slots = pa.slot_mapping(torch.from_numpy(hist.cu).to(dev), torch.from_numpy(hist.end_pos).to(dev),
                                 self.tables, hist.num_tokens, w.num_blocks)

@@ -40,12 +40,17 @@
  *                amax = max_d |x_d| (NaN elements ignored), inv = amax > 0 ? 127 / amax : 0,
  *                code_d = clamp(rint(x_d * inv), -127, 127) (a NaN product gives -127),
  *                scale = amax / 127;
- *            a reader uses code * scale.  Pool layout (block_size must be 16):
- *                cache[num_blocks][num_kv_heads][16 * head_dim + 64] bytes
- *            each (block, KV head) tile holding the 16 x head_dim codes (token-major, as in
- *            the other pools) and then 16 float32 scales, the scale of token t at float
- *            index 4 * (t % 4) + t / 4 (so the scales of tokens r, r+4, r+8, r+12 are one
- *            16-byte word).  Decode reads the codes as f16 and forms, per token, the
+ *            a reader uses code * scale.  Pool layout (block_size must be 16), key and value
+ *            pools differing:
+ *                key_cache[num_blocks][num_kv_heads][16 * head_dim + 128] bytes
+ *                value_cache[num_blocks][num_kv_heads][16][head_dim] bytes
+ *            each (block, KV head) key tile holding the 16 x head_dim key codes (token-major, as
+ *            in the other pools), then the 16 float32 key scales, then the 16 float32 value
+ *            scales of the same tokens; the value tile holds the value codes only.  Within each
+ *            group of 16 scales the scale of token t sits at float index 4 * (t % 4) + t / 4 (so
+ *            the scales of tokens r, r+4, r+8, r+12 are one 16-byte word).  Every tile is a
+ *            whole number of 128-byte lines, and both rows' scales travel with the key tile a
+ *            work-group reads anyway.  Decode reads the codes as f16 and forms, per token, the
  *            probability times the value scale in f16 (11 significant bits; p <= 256 with
  *            the kernel's lazy running max): value rows need amax below 32000, and
  *            products below 2^-14 keep only f16's subnormal precision.
@@ -77,9 +82,9 @@
  *     [0, min(max_context_len, max_blocks_per_seq * block_size)].  Results for such
  *     inputs are unspecified but no access leaves the buffers described here.
  *   - Supported now: block_size 16; head_dim 64 or 128; gqa_group 1, 2, 4, 8 or 16;
- *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, FP8_E4M3), and
- *     (BF16, INT8) for the decode calls without append; packed (varlen) batches take
- *     (BF16, BF16) and (BF16, FP8_E5M2).
+ *     (query, cache) types (F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, FP8_E4M3) and
+ *     (BF16, INT8) for the decode calls; packed (varlen) batches take (BF16, BF16) and
+ *     (BF16, FP8_E5M2).
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -93,7 +98,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum {
   PA_OK = 0,
@@ -155,7 +160,7 @@ pa_status_t paged_kv_slot_mapping(int32_t* slot_mapping, const int32_t* cu_token
  *   (src, cache) in {(F32, F32), (BF16, BF16), (BF16, FP8_E5M2), (BF16, INT8), (BF16,
  *   FP8_E4M3)}; a same-type write copies bits, the E5M2 cast is round-to-nearest-even, an INT8
  *   or FP8_E4M3 write quantises each (token, KV head) row and stores its codes and scale (see
- *   above; block_size 16 and head_dim 64 or 128 for these).
+ *   above: both scales go to the key pool; block_size 16 and head_dim 64 or 128 for these).
  *   Two rows with the same slot in one call race: the stored row is unspecified.
  */
 pa_status_t kv_cache_write(const void* key, const void* value, void* key_cache,
@@ -291,13 +296,12 @@ pa_status_t paged_attention_decode_reduce(void* out, const int32_t* context_lens
  * The newest token of sequence s sits at position L-1 (L = context_lens[s], which counts
  * it).  Its rows key[s], value[s] ([num_kv_heads][head_dim], q_dtype, dense, 16-byte
  * aligned) are stored at slot block_tables[s][(L-1)/B]*B + (L-1)%B of the pools (cast to
- * E5M2 when kv_dtype is FP8_E5M2, quantised to codes and a row scale when it is FP8_E4M3,
- * exactly as kv_cache_write does), and the attention is paged_attention_decode over all L
- * tokens.  The result, pools and output, is bit-identical to paged_kv_slot_mapping +
+ * E5M2 when kv_dtype is FP8_E5M2, quantised to codes and a row scale when it is INT8 or
+ * FP8_E4M3, exactly as kv_cache_write does), and the attention is paged_attention_decode over
+ * all L tokens.  The result, pools and output, is bit-identical to paged_kv_slot_mapping +
  * kv_cache_write + paged_attention_decode with the same partition size.  A sequence with
  * L = 0 appends nothing.  A slot whose table entry is outside [0, num_blocks) is not
- * written.  INT8 pools are not supported here (PA_ERR_UNSUPPORTED): write their rows with
- * kv_cache_write.
+ * written.
  *
  * flags: PA_APPEND_SKIP_REDUCE -- run only the streaming pass; the caller then runs
  *        paged_attention_decode_reduce (same arguments) when a sequence is split.
@@ -429,7 +433,8 @@ pa_status_t pa_bm_stats(const pa_block_manager* manager, int32_t* free_blocks, i
  * pairs[2i] -> block pairs[2i+1] (every KV head, every slot).  Carries out the copies that
  * pa_bm_append reports.  pairs: device int32 [2 * num_pairs]; a pair with an entry outside
  * [0, num_blocks) or src == dst is skipped; two pairs with the same destination race.
- * cache_dtype: any pool type (bytes are copied; an INT8 or FP8_E4M3 block carries its scales).
+ * cache_dtype: any pool type (bytes are copied; an INT8 or FP8_E4M3 key block carries both rows'
+ * scales).
  */
 pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,

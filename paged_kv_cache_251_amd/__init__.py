@@ -18,15 +18,15 @@ from .binding import (  # noqa: F401
     alloc_workspace,
     auto_partition,
     copy_blocks,
-    int8_pool_split,
     int8_scale_order,
     kv_cache_write,
     lib,
-    new_int8_pool,
+    new_scaled_pools,
     paged_attention_decode,
     paged_attention_decode_append,
     paged_attention_decode_static,
     paged_attention_varlen,
+    scaled_pool_split,
     slot_mapping,
     workspace_size,
 )

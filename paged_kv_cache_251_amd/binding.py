@@ -19,7 +19,8 @@ LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(_HERE, "libpagedattn.so"
 
 PA_F32, PA_BF16, PA_FP8_E5M2, PA_INT8, PA_FP8_E4M3 = 0, 1, 2, 3, 4
 INT8_BLOCK = 16  # tokens per block of a scaled (INT8 / FP8_E4M3) pool
-# torch element types that carry the bytes of a scaled pool: [nb, Hkv, 16 * D + 64]
+# torch element types that carry the bytes of a scaled pool pair: key pool [nb, Hkv, 16 * D + 128]
+# (codes, then the key and the value scales), value pool [nb, Hkv, 16, D] (codes)
 SCALED_POOL_TYPES = {torch.int8: PA_INT8, torch.float8_e4m3fn: PA_FP8_E4M3}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "device error",
           5: "out of blocks"}
@@ -157,34 +158,45 @@ def dtype_code(t: torch.Tensor) -> int:
 
 
 def _pool_dims(cache: torch.Tensor):
-    """(num_blocks, num_kv_heads, block_size, head_dim) of a pool: [nb, Hkv, B, D] of its element
-    type, or for a scaled pool (torch.int8: INT8 codes, torch.float8_e4m3fn: E4M3 codes) bytes
-    [nb, Hkv, 16 * D + 64] (codes, then 16 float32 scales)."""
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a key pool: [nb, Hkv, B, D] of its element
+    type, or for a scaled key pool (torch.int8: INT8 codes, torch.float8_e4m3fn: E4M3 codes) bytes
+    [nb, Hkv, 16 * D + 128] (codes, then 16 float32 key scales and 16 float32 value scales)."""
     if cache.dtype in SCALED_POOL_TYPES:
-        _expect(cache.dim() == 3 and (cache.shape[2] - 64) % INT8_BLOCK == 0 and cache.shape[2] > 64,
-                "a scaled pool is [num_blocks, Hkv, 16 * D + 64] bytes")
-        return cache.shape[0], cache.shape[1], INT8_BLOCK, (cache.shape[2] - 64) // INT8_BLOCK
+        _expect(cache.dim() == 3 and (cache.shape[2] - 128) % INT8_BLOCK == 0 and cache.shape[2] > 128,
+                "a scaled key pool is [num_blocks, Hkv, 16 * D + 128] bytes")
+        return cache.shape[0], cache.shape[1], INT8_BLOCK, (cache.shape[2] - 128) // INT8_BLOCK
     _expect(cache.dim() == 4, "a pool is [num_blocks, Hkv, block_size, D]")
     return tuple(cache.shape)
 
 
-def new_int8_pool(num_blocks: int, num_kv_heads: int, head_dim: int, device,
-                  dtype: torch.dtype = torch.int8) -> torch.Tensor:
-    """Zeroed scaled pool (codes and scales) for num_blocks blocks of 16 tokens; dtype torch.int8
+def _check_pools(key_cache: torch.Tensor, value_cache: torch.Tensor):
+    """Dims of a key/value pool pair (see _pool_dims); the value pool of a scaled pair is
+    [nb, Hkv, 16, D] of the same type."""
+    dims = _pool_dims(key_cache)
+    _expect(value_cache.dtype == key_cache.dtype, "pools differ in type")
+    want = tuple(dims) if key_cache.dtype in SCALED_POOL_TYPES else tuple(key_cache.shape)
+    _expect(tuple(value_cache.shape) == want, f"value pool must be {want}, got {tuple(value_cache.shape)}")
+    return dims
+
+
+def new_scaled_pools(num_blocks: int, num_kv_heads: int, head_dim: int, device, dtype: torch.dtype = torch.int8):
+    """Zeroed scaled pool pair for num_blocks blocks of 16 tokens: the key pool [nb, Hkv, 16 * D + 128]
+    (codes, key scales, value scales) and the value pool [nb, Hkv, 16, D] (codes); dtype torch.int8
     (INT8 codes) or torch.float8_e4m3fn (FP8 E4M3 codes)."""
     _expect(dtype in SCALED_POOL_TYPES, "a scaled pool is torch.int8 or torch.float8_e4m3fn")
-    return torch.zeros((num_blocks, num_kv_heads, INT8_BLOCK * head_dim + 64), dtype=torch.int8,
-                       device=device).view(dtype)
+    k = torch.zeros((num_blocks, num_kv_heads, INT8_BLOCK * head_dim + 128), dtype=torch.int8, device=device)
+    v = torch.zeros((num_blocks, num_kv_heads, INT8_BLOCK, head_dim), dtype=torch.int8, device=device)
+    return k.view(dtype), v.view(dtype)
 
 
-def int8_pool_split(pool: torch.Tensor):
-    """Views of a scaled pool: codes [nb, Hkv, 16, D] (the pool's type) and the scales
-    [nb, Hkv, 16] (float32) in their stored order -- the scale of token t at index
+def scaled_pool_split(key_pool: torch.Tensor):
+    """Views of a scaled key pool: key codes [nb, Hkv, 16, D] (the pool's type), key scales and value
+    scales [nb, Hkv, 16] (float32) in their stored order -- the scale of token t at index
     4 * (t % 4) + t // 4."""
-    nb, hkv, bs, d = _pool_dims(pool)
-    codes = pool[:, :, : bs * d].view(nb, hkv, bs, d)
-    scales = pool.view(torch.int8)[:, :, bs * d:].view(torch.float32)
-    return codes, scales
+    nb, hkv, bs, d = _pool_dims(key_pool)
+    codes = key_pool[:, :, : bs * d].view(nb, hkv, bs, d)
+    scales = key_pool.view(torch.int8)[:, :, bs * d:].view(torch.float32)
+    return codes, scales[:, :, :bs], scales[:, :, bs:]
 
 
 def int8_scale_order() -> list:
@@ -224,9 +236,8 @@ def kv_cache_write(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tens
     _dev(key, value, key_cache, value_cache, slot_mapping)
     _int32(slot_mapping)
     t, hkv, d = key.shape
-    nb, phkv, bs, pd = _pool_dims(key_cache)
+    nb, phkv, bs, pd = _check_pools(key_cache, value_cache)
     _expect(value.shape == key.shape and value.dtype == key.dtype, "key and value rows differ")
-    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
     _expect(phkv == hkv and pd == d, "rows and pools disagree on Hkv / D")
     _expect(slot_mapping.shape == (t,), "slot_mapping must be [num_tokens]")
     _check("kv_cache_write", lib().kv_cache_write(
@@ -258,8 +269,7 @@ def paged_attention_decode(query: torch.Tensor, key_cache: torch.Tensor, value_c
     _dev(query, key_cache, value_cache, block_tables, context_lens)
     _int32(block_tables, context_lens)
     n, hq, d = query.shape
-    nb, hkv, bs, pd = _pool_dims(key_cache)
-    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    nb, hkv, bs, pd = _check_pools(key_cache, value_cache)
     _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
     _expect(block_tables.dim() == 2 and block_tables.shape[0] == n and context_lens.shape == (n,),
             "block_tables [N, max_blocks], context_lens [N]")
@@ -292,8 +302,7 @@ def paged_attention_decode_static(query: torch.Tensor, key_cache: torch.Tensor, 
     _dev(query, key_cache, value_cache, block_tables, context_lens)
     _int32(block_tables, context_lens)
     n, hq, d = query.shape
-    nb, hkv, bs, pd = _pool_dims(key_cache)
-    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    nb, hkv, bs, pd = _check_pools(key_cache, value_cache)
     _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
     _expect(block_tables.dim() == 2 and block_tables.shape[0] == n and context_lens.shape == (n,),
             "block_tables [N, max_blocks], context_lens [N]")
@@ -319,8 +328,7 @@ def paged_attention_decode_append(query: torch.Tensor, key: torch.Tensor, value:
     _dev(query, key, value, key_cache, value_cache, block_tables, context_lens)
     _int32(block_tables, context_lens)
     n, hq, d = query.shape
-    nb, hkv, bs, pd = _pool_dims(key_cache)
-    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
+    nb, hkv, bs, pd = _check_pools(key_cache, value_cache)
     _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
     _expect(key.shape == (n, hkv, d) and value.shape == key.shape, "key/value rows must be [N, Hkv, D]")
     _expect(key.dtype == query.dtype and value.dtype == query.dtype, "key/value rows take the query dtype")
@@ -351,9 +359,8 @@ def paged_attention_varlen(query: torch.Tensor, key_cache: torch.Tensor, value_c
     _dev(query, key_cache, value_cache, cu_seqlens_q, context_lens, block_tables)
     _int32(cu_seqlens_q, context_lens, block_tables)
     total_q, hq, d = query.shape
-    nb, hkv, bs, pd = _pool_dims(key_cache)
+    nb, hkv, bs, pd = _check_pools(key_cache, value_cache)
     n = context_lens.shape[0]
-    _expect(value_cache.shape == key_cache.shape and value_cache.dtype == key_cache.dtype, "pools differ")
     _expect(pd == d and hq % hkv == 0, "query and pools disagree on D / heads")
     _expect(cu_seqlens_q.shape == (n + 1,) and block_tables.dim() == 2 and block_tables.shape[0] == n,
             "cu_seqlens_q [N+1], context_lens [N], block_tables [N, max_blocks]")
@@ -448,8 +455,7 @@ def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor, pairs: torch
     """Carry out block copies [(src, dst)] (int32 [n, 2] on the GPU) in both pools."""
     _dev(key_cache, value_cache, pairs)
     _int32(pairs)
-    _expect(key_cache.shape == value_cache.shape and key_cache.dtype == value_cache.dtype, "pools differ")
-    nb, hkv, bs, d = _pool_dims(key_cache)
+    nb, hkv, bs, d = _check_pools(key_cache, value_cache)
     _check("paged_kv_copy_blocks", lib().paged_kv_copy_blocks(key_cache.data_ptr(), value_cache.data_ptr(),
                                                                pairs.data_ptr(), pairs.numel() // 2, hkv, d, bs, nb,
                                                                dtype_code(key_cache), _stream()))

@@ -426,8 +426,6 @@ pa_status_t paged_attention_decode_append(void* out, const void* query, const vo
                                   max_context_len, scale, q_dtype, kv_dtype, partition_size, workspace,
                                   workspace_bytes, true);
   if (st != PA_OK) return st;
-  if (kv_dtype == PA_INT8)
-    return fail(PA_ERR_UNSUPPORTED, "%s: INT8 pools are written by kv_cache_write (no fused append)", fn);
   if (num_seqs == 0) return ok();
   if (!key || !value) return fail(PA_ERR_INVALID_ARGUMENT, "%s: null key/value row pointer", fn);
   if (!aligned(key, 16) || !aligned(value, 16))
@@ -504,16 +502,19 @@ pa_status_t paged_kv_copy_blocks(void* key_cache, void* value_cache, const int32
   if (scaled_dtype(cache_dtype) && block_size != 16)
     return fail(PA_ERR_UNSUPPORTED, "%s: an INT8 / FP8_E4M3 pool takes block_size 16", fn);
   const size_t elem = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
-  // a scaled tile carries one float32 scale per token after its codes
-  const size_t row_bytes = static_cast<size_t>(head_dim) * elem + (scaled_dtype(cache_dtype) ? 4 : 0);
-  const size_t block_bytes = static_cast<size_t>(num_kv_heads) * block_size * row_bytes;
-  if (block_bytes % 16 != 0) return fail(PA_ERR_UNSUPPORTED, "%s: a block of %zu bytes is not a multiple of 16", fn, block_bytes);
+  // a scaled key tile carries a key and a value float32 scale per token after its codes
+  const size_t v_block_bytes = static_cast<size_t>(num_kv_heads) * block_size * head_dim * elem;
+  const size_t k_block_bytes =
+      v_block_bytes + (scaled_dtype(cache_dtype) ? static_cast<size_t>(num_kv_heads) * block_size * 8 : 0);
+  if (k_block_bytes % 16 != 0 || v_block_bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: a block of %zu bytes is not a multiple of 16", fn, v_block_bytes);
   if (num_pairs == 0) return ok();
   if (!key_cache || !value_cache || !pairs) return fail(PA_ERR_INVALID_ARGUMENT, "%s: null pointer", fn);
   if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(pairs, 4))
     return fail(PA_ERR_INVALID_ARGUMENT, "%s: caches must be 16-byte aligned", fn);
-  return device_status(pa::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, block_bytes, num_blocks, stream),
-                       fn);
+  return device_status(
+      pa::launch_copy_blocks(key_cache, value_cache, pairs, num_pairs, k_block_bytes, v_block_bytes, num_blocks, stream),
+      fn);
 }
 
 }  // extern "C"

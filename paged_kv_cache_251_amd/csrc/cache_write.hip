@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void cache_write_q8_kernel(const uint4* __rest
                                                              const int32_t* __restrict__ slots, int32_t num_tokens,
                                                              int32_t num_kv_heads, int32_t num_blocks) {
   constexpr int LPR = D / 8;  // lanes per row; divides 64, so a row never straddles waves
-  constexpr int TILE = TileStride<KV, D>::value;
+  constexpr int KTILE = KTileStride<KV, D>::value, VTILE = VTileStride<KV, D>::value;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t total = (size_t)num_tokens * num_kv_heads * LPR;
   if (i >= total) return;  // total is a multiple of LPR: a row's lanes leave together
@@ -118,9 +118,10 @@ __global__ __launch_bounds__(256) void cache_write_q8_kernel(const uint4* __rest
   const int slot = slots[t];
   if (slot < 0 || slot >= num_blocks * 16) return;  // same slot on every lane of the row
   const int r = slot & 15;
-  const size_t tile = ((size_t)(slot >> 4) * num_kv_heads + h) * TILE;
+  const size_t unit = (size_t)(slot >> 4) * num_kv_heads + h;
+  const size_t ktile = unit * KTILE;  // holds the key codes, then the key and the value scales
 
-  auto quantize = [&](uint4 w, uint8_t* pool) {
+  auto quantize = [&](uint4 w, uint8_t* codes, float* scale) {
     const uint32_t words[4] = {w.x, w.y, w.z, w.w};
     float x[8];
     int key_max = -1;
@@ -137,11 +138,12 @@ __global__ __launch_bounds__(256) void cache_write_q8_kernel(const uint4* __rest
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) packed[k >> 2] |= q8_code<KV>(x[k], inv) << (8 * (k & 3));
-    *reinterpret_cast<uint2*>(pool + tile + (size_t)r * D + (size_t)c * 8) = make_uint2(packed[0], packed[1]);
-    if (c == 0) *reinterpret_cast<float*>(pool + tile + q8_scale_offset<D>(r)) = amax / Q8Range<KV>::value;
+    *reinterpret_cast<uint2*>(codes + (size_t)r * D + (size_t)c * 8) = make_uint2(packed[0], packed[1]);
+    if (c == 0) *scale = amax / Q8Range<KV>::value;
   };
-  quantize(key[i], key_cache);
-  quantize(value[i], value_cache);
+  float* kscale = reinterpret_cast<float*>(key_cache + ktile + q8_scale_offset<D>(r));
+  quantize(key[i], key_cache + ktile, kscale);
+  quantize(value[i], value_cache + unit * VTILE, kscale + kValueScaleOffset / 4);
 }
 
 hipError_t launch_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
@@ -185,21 +187,23 @@ hipError_t launch_cache_write(const void* key, const void* value, void* key_cach
 // Whole-block copies of both pools (copy on write of a shared, partly filled block): work-group
 // (pair, pool) copies one block of `block_bytes` with 16-byte loads and stores.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* key_cache, uint8_t* value_cache,
-                                                          const int32_t* pairs, size_t block_bytes, int32_t num_blocks) {
+                                                          const int32_t* pairs, size_t k_block_bytes,
+                                                          size_t v_block_bytes, int32_t num_blocks) {
   const int32_t src = pairs[2 * (size_t)blockIdx.x], dst = pairs[2 * (size_t)blockIdx.x + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
   uint8_t* base = blockIdx.y == 0 ? key_cache : value_cache;
+  const size_t block_bytes = blockIdx.y == 0 ? k_block_bytes : v_block_bytes;
   const uint4* from = reinterpret_cast<const uint4*>(base + (size_t)src * block_bytes);
   uint4* to = reinterpret_cast<uint4*>(base + (size_t)dst * block_bytes);
   for (size_t i = threadIdx.x; i < block_bytes / 16; i += 256) to[i] = from[i];
 }
 
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
-                              size_t block_bytes, int32_t num_blocks, hipStream_t stream) {
+                              size_t k_block_bytes, size_t v_block_bytes, int32_t num_blocks, hipStream_t stream) {
   if (num_pairs <= 0) return hipSuccess;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, stream,
-                     static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache), pairs, block_bytes,
-                     num_blocks);
+                     static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache), pairs, k_block_bytes,
+                     v_block_bytes, num_blocks);
   return hipGetLastError();
 }
 

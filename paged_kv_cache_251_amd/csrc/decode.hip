@@ -21,9 +21,10 @@
 //    and the denominator, and it makes the rescale branch rare.
 //  * Probabilities reach the PV lanes by DPP row broadcast; V is accumulated in fp32
 //    (f32 / bf16 caches) or with f16 dot2 over token pairs (E5M2, INT8 and E4M3 caches, whose
-//    codes widen exactly to f16).  An INT8 or E4M3 tile ends in its 16 row scales, ordered so
-//    that one 16-byte load gives a lane the scales of its row's four tokens: the key scale
-//    multiplies the finished dot product, the value scale the probability (in f16).
+//    codes widen exactly to f16).  An INT8 or E4M3 key tile ends in its 16 key scales and then
+//    the 16 value scales of the same tokens, each group ordered so that one 16-byte load gives a
+//    lane the scales of its row's four tokens: the key scale multiplies the finished dot
+//    product, the value scale the probability (in f16).
 //  * Rows, then waves, are merged at the end; a single partition writes the output,
 //    several write (o/l, m, l) to the workspace for the reduce kernel.
 #include <atomic>
@@ -36,7 +37,7 @@
 namespace pa {
 
 template <int KV, int D, int G, int W>
-__global__ __launch_bounds__(64 * W, (KV == KV_I8 && G <= 4) ? PA_I8_WAVES_PER_EU : 1) void decode_partition_kernel(
+__global__ __launch_bounds__(64 * W) void decode_partition_kernel(
     const DecodeParams p) {
   __shared__ int sm_i[DecodeSmem<G, D, W>::INTS];
   __shared__ float sm_f[DecodeSmem<G, D, W>::FLOATS];

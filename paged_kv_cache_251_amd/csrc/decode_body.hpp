@@ -87,15 +87,10 @@ struct DecodeTile {
   static constexpr int QDW = KV == KV_F32 ? EPL : EPL / 2;  // q dwords per head per lane
   static constexpr bool F16_Q = KV == KV_E5M2 || Scaled<KV>::value;  // bf16 query widened to f16
   static constexpr int SCW = Scaled<KV>::value ? 4 : 1;              // scale dwords per lane per tile
-  static constexpr int TILE = TileStride<KV, D>::value;        // bytes per (block, KV head)
+  static constexpr int KTILE = KTileStride<KV, D>::value;      // key pool bytes per (block, KV head)
+  static constexpr int VTILE = VTileStride<KV, D>::value;      // value pool bytes per (block, KV head)
 };
 
-// The INT8 kernels with up to 4 heads per group are held to 128 VGPRs (4 waves per SIMD instead
-// of 3; the few values spilled are outside the loop); larger groups need the registers.  The E4M3
-// kernels measured faster without the limit (they would spill more).
-#ifndef PA_I8_WAVES_PER_EU
-#define PA_I8_WAVES_PER_EU 4
-#endif
 
 // LDS of one decode work-group: the ranking arrays (ints) and the wave merge (floats).
 template <int G, int D, int W>
@@ -170,13 +165,11 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int bx, int b
   // b_new then comes from the new row instead of the cache (no read-after-write inside
   // the launch).  Lane (row, col) keeps columns col*EPL .. col*EPL+EPL-1 in cache format.
   const int pos_new = L - 1;
-  // (INT8 pools do not append: the kernel is held to 128 VGPRs, and the splice's registers would
-  // spill inside the tile loop)
-  const bool appending = KV != KV_I8 && p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
+  const bool appending = p.key_new != nullptr && pos_new >= t0 && pos_new < t1;
   const int b_new = appending ? pos_new / 16 : -1;
   const int r_new = pos_new & 15;
   uint32_t knew[NDW], vnew[NDW];
-  constexpr bool RAW = KV == KV_E5M2 || KV == KV_E4M3;  // the new row arrives as bf16 and is cast
+  constexpr bool RAW = KV == KV_E5M2 || Scaled<KV>::value;  // the new row arrives as bf16 and is cast
   uint32_t kraw[RAW ? 2 * NDW : 1], vraw[RAW ? 2 * NDW : 1];
   if (appending) {
     const size_t roff = ((size_t)s * p.num_kv_heads + g) * D + (size_t)col * EPL;  // element offset
@@ -186,18 +179,18 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int bx, int b
     } else if constexpr (KV == KV_BF16) {
       load_dw<NDW>(knew, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
       load_dw<NDW>(vnew, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
-    } else if constexpr (RAW) {  // E5M2, E4M3: bf16 rows
+    } else if constexpr (RAW) {  // E5M2, INT8, E4M3: bf16 rows
       load_dw<2 * NDW>(kraw, reinterpret_cast<const uint16_t*>(p.key_new) + roff);
       load_dw<2 * NDW>(vraw, reinterpret_cast<const uint16_t*>(p.value_new) + roff);
     }
   }
   // Once the first tile is in flight: cast the new row to the cache type (bf16 -> E5M2 is
-  // the cache write's own cast; E4M3 rows are quantised with the cache write's rule, the row's
-  // amax reduced over the 16 lanes of a DPP row) and store it at its slot.
-  float kscale = 0.f, vscale = 0.f;  // E4M3: the new rows' scales
+  // the cache write's own cast; INT8 and E4M3 rows are quantised with the cache write's rule, the
+  // row's amax reduced over the 16 lanes of a DPP row) and store it at its slot.
+  float kscale = 0.f, vscale = 0.f;  // INT8, E4M3: the new rows' scales
   auto finish_append = [&]() {
     if (!appending) return;
-    if constexpr (KV == KV_E4M3) {
+    if constexpr (Scaled<KV>::value) {
       auto quantize_row = [&](const uint32_t(&raw)[2 * NDW], uint32_t(&codes)[NDW]) -> float {
         int key_max = -1;
 #pragma unroll
@@ -226,18 +219,19 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int bx, int b
     }
     const int phys = load_invariant(p.block_tables + (size_t)s * p.max_blocks_per_seq + b_new);
     if (wave == 0 && row == 0 && phys >= 0 && phys < p.num_blocks) {
-      const size_t tile = ((size_t)phys * p.num_kv_heads + g) * T::TILE;
-      const size_t dst = tile + ((size_t)r_new * D + (size_t)col * EPL) * SZ;
-      if constexpr (KV == KV_E4M3) {
+      const size_t unit = (size_t)phys * p.num_kv_heads + g;
+      const size_t ktile = unit * T::KTILE, vtile = unit * T::VTILE;
+      const size_t in_tile = ((size_t)r_new * D + (size_t)col * EPL) * SZ;
+      if constexpr (Scaled<KV>::value) {
         if (col == 0) {
-          *reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + tile + q8_scale_offset<D>(r_new)) =
-              kscale;
-          *reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p.value_cache_w) + tile + q8_scale_offset<D>(r_new)) =
-              vscale;
+          float* sc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + ktile +
+                                               q8_scale_offset<D>(r_new));
+          sc[0] = kscale;
+          sc[kValueScaleOffset / 4] = vscale;
         }
       }
-      uint32_t* kc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + dst);
-      uint32_t* vc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.value_cache_w) + dst);
+      uint32_t* kc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + ktile + in_tile);
+      uint32_t* vc = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(p.value_cache_w) + vtile + in_tile);
 #pragma unroll
       for (int j = 0; j < NDW; ++j) {
         kc[j] = knew[j];
@@ -295,7 +289,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int bx, int b
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.value_cache);
   const size_t lane_off = ((size_t)row * D + (size_t)col * EPL) * SZ;
 
-  // INT8 scales of this lane's row: tokens row, row+4, row+8, row+12 of the tile
+  // scales of this lane's row (INT8, E4M3): tokens row, row+4, row+8, row+12 of the tile; the key
+  // scales, then 64 bytes further the value scales, both in the key pool's tile
   const size_t scale_off = (size_t)16 * D + (size_t)row * 16;
 
   auto load_tile = [&](int b, uint32_t (&kd)[NL][NDW], uint32_t (&vd)[NL][NDW], uint32_t (&ks)[SCW],
@@ -303,14 +298,14 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int bx, int b
     int phys = load_invariant(table + b);
     const bool ok = phys >= 0 && phys < p.num_blocks;
     phys = ok ? phys : 0;
-    const size_t tile = ((size_t)phys * p.num_kv_heads + g) * T::TILE;
-    const size_t off = tile + lane_off;
+    const size_t unit = (size_t)phys * p.num_kv_heads + g;
+    const size_t ktile = unit * T::KTILE, vtile = unit * T::VTILE;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(kd[i], kbase + off + (size_t)i * 4 * D * SZ);
-    if constexpr (Scaled<KV>::value) load_dw<4, PA_NT_LOADS>(ks, kbase + tile + scale_off);
+    for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(kd[i], kbase + ktile + lane_off + (size_t)i * 4 * D * SZ);
+    if constexpr (Scaled<KV>::value) load_dw<4, PA_NT_LOADS>(ks, kbase + ktile + scale_off);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(vd[i], vbase + off + (size_t)i * 4 * D * SZ);
-    if constexpr (Scaled<KV>::value) load_dw<4, PA_NT_LOADS>(vs, vbase + tile + scale_off);
+    for (int i = 0; i < NL; ++i) load_dw<NDW, PA_NT_LOADS>(vd[i], vbase + vtile + lane_off + (size_t)i * 4 * D * SZ);
+    if constexpr (Scaled<KV>::value) load_dw<4, PA_NT_LOADS>(vs, kbase + ktile + scale_off + kValueScaleOffset);
     __builtin_amdgcn_sched_barrier(0);  // issue the tile before any math that follows
     return ok;
   };
@@ -328,7 +323,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int bx, int b
           kd[i][j] = mine ? knew[j] : kd[i][j];
           vd[i][j] = mine ? vnew[j] : vd[i][j];
         }
-        if constexpr (KV == KV_E4M3) {
+        if constexpr (Scaled<KV>::value) {
           ks[i] = mine ? as_u32(kscale) : ks[i];
           vs[i] = mine ? as_u32(vscale) : vs[i];
         }

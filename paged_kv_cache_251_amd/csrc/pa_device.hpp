@@ -25,11 +25,18 @@ struct KvBytes<KV_E4M3> { static constexpr int value = 1; };
 template <int KV>
 struct Scaled { static constexpr bool value = KV == KV_I8 || KV == KV_E4M3; };
 
-// Bytes from the start of one (block, KV head) tile of 16 x D elements to the next: the tile,
-// and for the scaled kinds the 16 float32 scales that follow it.
+// Bytes from the start of one (block, KV head) tile of 16 x D elements to the next.  Key pool:
+// the codes, and for the scaled kinds the 16 float32 key scales and then the 16 float32 value
+// scales of the same tokens (128 bytes, so every tile is a whole number of 128-byte lines and a
+// work-group reading a tile never fetches a line that another tile shares).  Value pool: the
+// codes only.
 template <int KV, int D>
-struct TileStride {
-  static constexpr int value = 16 * D * KvBytes<KV>::value + (Scaled<KV>::value ? 64 : 0);
+struct KTileStride {
+  static constexpr int value = 16 * D * KvBytes<KV>::value + (Scaled<KV>::value ? 128 : 0);
+};
+template <int KV, int D>
+struct VTileStride {
+  static constexpr int value = 16 * D * KvBytes<KV>::value;
 };
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -260,13 +267,14 @@ __device__ __forceinline__ uint32_t q8_code(float x, float inv) {
     return f32_to_e4m3_sat(x * inv);
   }
 }
-// byte offset, inside a scaled tile of head_dim D, of the scale of token r of the block: token
-// r's scale sits at index 4(r mod 4) + r/4, so a lane of DPP row q reads the scales of its
-// tokens q, q+4, q+8, q+12 with one 16-byte load
+// byte offset, inside a scaled key tile of head_dim D, of the key scale of token r of the block
+// (its value scale sits 64 bytes further): token r's scale sits at index 4(r mod 4) + r/4, so a
+// lane of DPP row q reads the scales of its tokens q, q+4, q+8, q+12 with one 16-byte load
 template <int D>
 __device__ __forceinline__ int q8_scale_offset(int r) {
   return 16 * D + 4 * (4 * (r & 3) + (r >> 2));
 }
+constexpr int kValueScaleOffset = 64;  // value scales after the key scales, in the key tile
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,

@@ -92,9 +92,10 @@ hipError_t launch_slot_mapping(int32_t* slots, const int32_t* cu, const int32_t*
                                int32_t num_tokens, int32_t block_size, int32_t num_blocks,
                                hipStream_t stream);
 
-// Copy whole blocks src -> dst of both pools (pairs: device int32 [2 * num_pairs]).
+// Copy whole blocks src -> dst of both pools (pairs: device int32 [2 * num_pairs]); a key block
+// and a value block may differ in size (the scaled kinds keep both rows' scales in the key pool).
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, const int32_t* pairs, int32_t num_pairs,
-                              size_t block_bytes, int32_t num_blocks, hipStream_t stream);
+                              size_t k_block_bytes, size_t v_block_bytes, int32_t num_blocks, hipStream_t stream);
 
 hipError_t launch_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
                               const int32_t* slots, int32_t num_tokens, int32_t num_kv_heads,

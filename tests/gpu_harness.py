@@ -40,30 +40,39 @@ def to_raw(t: torch.Tensor, dtype: str) -> np.ndarray:
     return t.numpy()
 
 
-def poisoned_pool(w, dtype: str | None = None) -> torch.Tensor:
+def poisoned_pool(w, dtype: str | None = None, which: str = "k") -> torch.Tensor:
+    """A pool with every word poisoned (NaN patterns).  A scaled pair's key pool holds, per (block,
+    head), the codes and then the key and the value scales; its value pool the codes only."""
     dtype = dtype or w.kv_dtype
     bits = POISON_BITS[dtype]
-    if dtype in SCALED:  # codes then 16 float32 scales per (block, head) tile; every word NaN
-        words = (w.num_blocks, w.num_kv_heads, (w.block_size * w.head_dim + 64) // 4)
+    if dtype in SCALED:
+        if which == "k":
+            words = (w.num_blocks, w.num_kv_heads, (w.block_size * w.head_dim + 128) // 4)
+            return torch.full(words, bits, dtype=torch.int32, device=DEV).view(SCALED[dtype])
+        words = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim // 4)
         return torch.full(words, bits, dtype=torch.int32, device=DEV).view(SCALED[dtype])
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
     t = torch.full(shape, bits, dtype=INT_VIEW[dtype], device=DEV)
     return t if dtype == "e5m2" else t.view(TORCH_STORAGE[dtype])
 
 
-def int8_canonical(pool: torch.Tensor):
-    """Scaled pool -> (codes [nb, B, Hkv, D] as raw bytes (uint8), scales [nb, B, Hkv] float32),
-    both in the oracle's layout and token order."""
-    codes, scales = pa.int8_pool_split(pool)
-    c = codes.view(torch.uint8).cpu().numpy().transpose(0, 2, 1, 3)
+def scaled_canonical(pk: torch.Tensor, pv: torch.Tensor) -> dict:
+    """Scaled pool pair -> {"k": (codes, scales), "v": (codes, scales)}: codes [nb, B, Hkv, D] as raw
+    bytes (uint8), scales [nb, B, Hkv] float32, in the oracle's layout and token order (both rows'
+    scales are read from the key pool)."""
+    kcodes, kscales, vscales = pa.scaled_pool_split(pk)
     slot_of_token = np.argsort(pa.int8_scale_order())  # stored slot -> token order
-    sc = scales.cpu().numpy()[:, :, slot_of_token]
-    return np.ascontiguousarray(c), np.ascontiguousarray(sc.transpose(0, 2, 1))
+    out = {}
+    for name, codes, scales in (("k", kcodes, kscales), ("v", pv, vscales)):
+        c = codes.view(torch.uint8).cpu().numpy().transpose(0, 2, 1, 3)
+        sc = scales.cpu().numpy()[:, :, slot_of_token]
+        out[name] = (np.ascontiguousarray(c), np.ascontiguousarray(sc.transpose(0, 2, 1)))
+    return out
 
 
 def oracle_int8_pools(w, phases=("all",), seqs=None):
     """Oracle state of a scaled (int8 / e4m3) workload: codes (raw bytes), scales (as
-    int8_canonical gives them, NaN scales where nothing was written) and the dequantised float64
+    scaled_canonical gives them, NaN scales where nothing was written) and the dequantised float64
     pools for the attention oracle."""
     quant, dequant = QUANT[w.kv_dtype]
     shape = (w.num_blocks, w.block_size, w.num_kv_heads)
@@ -99,8 +108,8 @@ class DeviceBatch:
         self.w = w
         self.tables = torch.from_numpy(w.block_tables).to(DEV)
         self.lens = torch.from_numpy(w.context_lens).to(DEV)
-        self.pk = poisoned_pool(w)
-        self.pv = poisoned_pool(w)
+        self.pk = poisoned_pool(w, which="k")
+        self.pv = poisoned_pool(w, which="v")
         self.slots = {}
         for ph in phases:
             self.write(ph, seqs)

@@ -46,7 +46,7 @@ def test_binding_signatures_cover_the_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pa_abi_version() == 4
+    assert lib.pa_abi_version() == 5
     assert lib.pa_status_string(5) == b"out of blocks"
     assert lib.pa_status_string(0) == b"ok"
     assert lib.pa_status_string(3) == b"workspace too small"
@@ -109,17 +109,15 @@ def test_cache_write_rejects_bad_arguments_on_host(lib):
 
 
 def test_int8_pool_is_rejected_where_unsupported(lib):
-    # the fused append: an INT8 pool is written by kv_cache_write; an FP8_E4M3 pool takes bf16
-    # queries and rows, and with them gets as far as the row pointers (checked on the host)
-    app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
-                                            64, 0.1, 1, 3, 0, 0, None, 0, None)
-    assert app == 2 and b"INT8" in lib.pa_last_error()
-    app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
-                                            64, 0.1, 0, 4, 0, 0, None, 0, None)
-    assert app == 2  # f32 queries
-    app = lib.paged_attention_decode_append(FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16, 8,
-                                            64, 0.1, 1, 4, 0, 0, None, 0, None)
-    assert app == 1 and b"key/value row" in lib.pa_last_error()
+    # the fused append: INT8 and FP8_E4M3 pools take bf16 queries and rows, and with them get as
+    # far as the row pointers (checked on the host)
+    for kd in (3, 4):
+        app = lib.paged_attention_decode_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16,
+                                                8, 64, 0.1, 0, kd, 0, 0, None, 0, None)
+        assert app == 2  # f32 queries
+        app = lib.paged_attention_decode_append(FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 4, FAKE, 2, 2, 2, 128, 16,
+                                                8, 64, 0.1, 1, kd, 0, 0, None, 0, None)
+        assert app == 1 and b"key/value row" in lib.pa_last_error()
     for kd in (0, 3, 4):  # packed batches take bf16 or FP8_E5M2 pools only
         var = lib.paged_attention_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 4, 2, 2, 2, 128, 16, 8, 64,
                                          0.1, 1, 1, kd, 0, None, 0, None)

@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import paged_kv_cache_251_amd as pa
-from gpu_harness import (DEV, QUANT, SCALED, DeviceBatch, assert_close, int8_canonical, oracle_int8_pools,
+from gpu_harness import (DEV, QUANT, SCALED, DeviceBatch, assert_close, oracle_int8_pools, scaled_canonical,
                          out_f64, poisoned_pool, to_device)
 from workloads import make_config, make_workload, queries
 
@@ -73,14 +73,15 @@ def test_scaled_cache_write_bit_exact(kind, D, hkv):
     nb = (T + 15) // 16 + 3
     w = make_workload([16], num_q_heads=hkv, num_kv_heads=hkv, head_dim=D, q_dtype="bf16", kv_dtype=kind,
                       pool=nb)
-    pk, pv = poisoned_pool(w), poisoned_pool(w)
-    before = pk.clone()
+    pk, pv = poisoned_pool(w, which="k"), poisoned_pool(w, which="v")
+    before = scaled_canonical(pk.clone(), pv.clone())
     slots = rng.permutation(nb * 16)[:T].astype(np.int32)
     slots[[4, 40]] = [-1, nb * 16 + 3]  # skipped rows
     pa.kv_cache_write(to_device(k, "bf16"), to_device(v, "bf16"), pk, pv, torch.from_numpy(slots).to(DEV))
     torch.cuda.synchronize()
-    for name, src, pool in (("k", k, pk), ("v", v, pv)):
-        codes, scales = int8_canonical(pool)
+    got = scaled_canonical(pk, pv)
+    for name, src in (("k", k), ("v", v)):
+        codes, scales = got[name]
         want_c, want_s = QUANT[kind][0](oracle.decode_storage(src, "bf16").astype(np.float32))
         want_c = _raw_codes(want_c)
         keep = slots >= 0
@@ -95,7 +96,7 @@ def test_scaled_cache_write_bit_exact(kind, D, hkv):
         # every slot not written keeps the poison (codes and scale)
         written = np.zeros((nb, 16), bool)
         written[blk, off] = True
-        pc, ps = int8_canonical(before)
+        pc, ps = before[name]
         assert np.array_equal(codes[~written], pc[~written]), name
         assert np.all(np.isnan(scales[~written])), name
 
@@ -104,8 +105,9 @@ def test_scaled_cache_write_bit_exact(kind, D, hkv):
 def test_scaled_copy_blocks_bit_exact(kind):
     rng = np.random.default_rng(5)
     nb, hkv, D = 24, 2, 128
-    kc = torch.from_numpy(rng.integers(-128, 128, size=(nb, hkv, 16 * D + 64), dtype=np.int8)).to(DEV)
-    vc = torch.from_numpy(rng.integers(-128, 128, size=(nb, hkv, 16 * D + 64), dtype=np.int8)).to(DEV)
+    # a key block holds the codes and both rows' scales, a value block the codes only
+    kc = torch.from_numpy(rng.integers(-128, 128, size=(nb, hkv, 16 * D + 128), dtype=np.int8)).to(DEV)
+    vc = torch.from_numpy(rng.integers(-128, 128, size=(nb, hkv, 16, D), dtype=np.int8)).to(DEV)
     pairs = np.array([[1, 20], [2, 21], [3, 3], [-1, 5], [7, 22]], np.int32)
     kx, vx = kc.cpu().clone(), vc.cpu().clone()
     for s, d in pairs:
@@ -121,8 +123,9 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 255, 256, 257, 511, 512, 513, 1000]
 
 def _check_pools_match(b, w, o, seqs=None):
     """The GPU-written pools hold exactly the oracle's codes and scales on every slot written."""
-    for name, pool in (("k", b.pk), ("v", b.pv)):
-        codes, scales = int8_canonical(pool)
+    got = scaled_canonical(b.pk, b.pv)
+    for name in ("k", "v"):
+        codes, scales = got[name]
         oc, os_, oset, _ = o[name]
         assert np.array_equal(codes[oset], oc[oset]), name
         assert np.array_equal(scales[oset].view(np.uint32), os_[oset].view(np.uint32)), name
@@ -206,11 +209,11 @@ def test_scaled_decode_full_size_sampled(kind):
 
 
 # ---------------------------------------------------------------- fused append on scaled pools
-@pytest.mark.parametrize("kind", ["e4m3"])
+@pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("D,G", [(128, 4), (128, 8), (64, 4), (64, 16)])
 def test_scaled_append_is_bit_identical_to_write_then_decode(kind, D, G):
-    """paged_attention_decode_append quantises each sequence's newest K/V row in the kernel (FP8
-    E4M3 pools; INT8 pools are written by kv_cache_write): the pools it leaves and its output equal,
+    """paged_attention_decode_append quantises each sequence's newest K/V row in the kernel (INT8
+    and FP8 E4M3 pools, with the cache write's rule): the pools it leaves and its output equal,
     byte for byte, the quantising kv_cache_write followed by the decode, and both match the
     oracle's codes, scales and attention."""
     from workloads import STORAGE, seq_kv
