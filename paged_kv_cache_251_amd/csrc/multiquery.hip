@@ -171,19 +171,25 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
     phys = t.ok ? phys : 0;
     const uint8_t* kb = kc + (size_t)phys * blk_bytes;
     const uint8_t* vb = vc + (size_t)phys * blk_bytes;
-    auto ld16 = [](const uint8_t* q) {  // 8 elements as bf16 (or f16 widened from E5M2)
+    // 8 elements as bf16 (or f16 widened from E5M2).  STREAM: a streaming load for data read once in
+    // whole lines (V: each load covers four whole rows).  A K load covers only a 64-byte half of
+    // each of its 16 rows' lines, the other half coming with the next k-step's load, so K is read
+    // through the cache normally: a streamed half-line could be gone before its second half is
+    // asked for, and the line would be fetched twice.
+    auto ld16 = [](const uint8_t* q, auto nt) {
+      constexpr bool STREAM = decltype(nt)::value;
       if constexpr (E8) {
-        const u32x2_t v = ld<u32x2_t, true>(q);  // streamed once
+        const u32x2_t v = ld<u32x2_t, STREAM>(q);
         return make_uint4(e5m2_pair_lo(v.x), e5m2_pair_hi(v.x), e5m2_pair_lo(v.y), e5m2_pair_hi(v.y));
       } else {
-        const u32x4_t v = ld<u32x4_t, true>(q);  // streamed once
+        const u32x4_t v = ld<u32x4_t, STREAM>(q);
         return make_uint4(v.x, v.y, v.z, v.w);
       }
     };
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) t.k[kk] = ld16(kb + k_off + 32 * kk * SZ);
+    for (int kk = 0; kk < KS; ++kk) t.k[kk] = ld16(kb + k_off + 32 * kk * SZ, std::false_type{});
 #pragma unroll
-    for (int u = 0; u < VLD; ++u) t.v[u] = ld16(vb + v_off[u]);
+    for (int u = 0; u < VLD; ++u) t.v[u] = ld16(vb + v_off[u], std::true_type{});
     __builtin_amdgcn_sched_barrier(0);  // issue the block before the math that follows
   };
 
