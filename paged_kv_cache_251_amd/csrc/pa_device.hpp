@@ -1,6 +1,8 @@
 // Device helpers shared by the libpagedattn kernels (gfx950, wave64).
 #pragma once
 
+#include <climits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -126,6 +128,30 @@ __device__ __forceinline__ constexpr int head_lane(int h) {
   return h * (16 / G);
 }
 
+// Reduction of an int over the 64 lanes of a wave, every lane receiving the result: an inclusive
+// scan over each 16-lane row by row_shr 1, 2, 4, 8, the row totals carried forward by row_bcast:15
+// and row_bcast:31 (rows 1, 3 and rows 2, 3), so that lane 63 ends with the whole wave's result.
+// Lanes whose DPP source lies outside the row, and rows the mask leaves out, combine the identity.
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i32(int x, int identity, Op op) {
+  x = op(x, __builtin_amdgcn_update_dpp(identity, x, 0x111, 0xF, 0xF, false));  // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(identity, x, 0x112, 0xF, 0xF, false));  // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(identity, x, 0x114, 0xF, 0xF, false));  // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(identity, x, 0x118, 0xF, 0xF, false));  // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(identity, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(identity, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
+}
+__device__ __forceinline__ int wave_sum_i32(int x) {
+  return wave_reduce_i32(x, 0, [](int a, int b) { return a + b; });
+}
+__device__ __forceinline__ int wave_min_i32(int x) {
+  return wave_reduce_i32(x, INT_MAX, [](int a, int b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+  return wave_reduce_i32(x, INT_MIN, [](int a, int b) { return a > b ? a : b; });
+}
+
 // Broadcast lane LANE of each 16-lane row to the whole row.
 template <int LANE>
 __device__ __forceinline__ float row_bcast(float v) {
@@ -147,6 +173,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = as_u32(f);
   uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
   return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? (((u >> 16) & 0x8000u) | 0x7FC0u) : r;
+}
+
+// Two binary32 -> two bfloat16 (low, high half), round to nearest even, by the hardware
+// conversion (v_cvt_pk_bf16_f32): finite values round as f32_to_bf16_rne does.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // bfloat16 (16-bit pattern) -> E5M2 code, round to nearest even, no saturation:

@@ -61,8 +61,8 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(uint4 w) {
 
 // E8: the cache holds E5M2 codes; they are widened to f16 on their way into LDS, the queries
 // are taken to f16 and the products run on the f16 MFMA (probabilities in f16).
-// LDS of one prefill work-group, in 16-bit elements: two K and two V tiles of 64 keys (double
-// buffer); the longest-first schedule's arrays use the same memory first.
+// LDS of one 4-wave group of a prefill work-group, in 16-bit elements: two K and two V tiles of 64
+// keys (double buffer).  The longest-first schedule's arrays use the same memory first.
 template <int D>
 struct PrefillSmem {
   static constexpr int KT = 64;
@@ -71,7 +71,10 @@ struct PrefillSmem {
   static constexpr int KBUF = KT * KP, VBUF = KT * VP;
   static constexpr int ELEMS = 2 * KBUF + 2 * VBUF;
   static constexpr int BYTES = 2 * ELEMS;
-  static_assert(BYTES >= (3 * kMaxScheduledSeqs + 1) * 4, "schedule arrays fit in the tiles");
+  // schedule: base, n, first row and index of every sequence with n >= 2, and a count per chunk
+  // of 64 sequences
+  static constexpr int SCHED_INTS = 4 * kMaxScheduledSeqs + kMaxScheduledSeqs / 64;
+  static_assert(BYTES >= SCHED_INTS * 4, "schedule arrays fit in the tiles");
 };
 
 // One work-group of the prefill rows: with p.sched_seqs > 0 the work-group of 1-D index bx takes
@@ -80,8 +83,9 @@ struct PrefillSmem {
 template <int D, int G, bool E8>
 __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int by, int bz, int grid_y,
                                              uint16_t* lds) {
-  constexpr int W = 4, NT = 2;            // waves; 16-row MFMA tiles per wave
-  constexpr int ROWS = W * NT * 16;       // query rows per work-group
+  constexpr int NW = 4;                   // waves
+  constexpr int NT = 2;                   // 16-row MFMA tiles per wave
+  constexpr int ROWS = 4 * NT * 16;       // query rows per work-group
   constexpr int TOKW = ROWS / G;          // tokens per work-group
   constexpr int KT = PrefillSmem<D>::KT;  // keys per LDS tile (4 cache blocks)
   constexpr int KS = D / 32;              // MFMA k-steps over head_dim
@@ -102,115 +106,154 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
     return L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
   };
 
-  int g, tile, s;
+  int g, tile, s, a, n, L;
   if (p.sched_seqs > 0) {
     // ---- longest-first schedule -------------------------------------------------------------
-    // Sequences with n >= 2 query tokens, compacted by wave 0: base = L - n, n.  Tile t of such
-    // a sequence has the sort key L - n + min(n, (t+1)*TOKW), strictly increasing in t (ties
-    // between sequences: lower compacted index first).
+    // Sequences with n >= 2 query tokens, compacted in index order: base = L - n, n, first row
+    // a, index.  Tile t of such a sequence has the sort key L - n + min(n, (t+1)*TOKW), strictly
+    // increasing in t (ties between sequences: lower compacted index first).
     int* sm_base = reinterpret_cast<int*>(lds);
     int* sm_n = sm_base + kMaxScheduledSeqs;
-    int* sm_seq = sm_n + kMaxScheduledSeqs;
-    int* sm_count = sm_seq + kMaxScheduledSeqs;
+    int* sm_a = sm_n + kMaxScheduledSeqs;
+    int* sm_seq = sm_a + kMaxScheduledSeqs;
+    int* sm_cnt = sm_seq + kMaxScheduledSeqs;  // per chunk of 64 sequences
     const int nseq = p.sched_seqs;
-    if (wave == 0) {
-      int cnt = 0;
-      for (int s0 = 0; s0 < nseq; s0 += 64) {
-        const int si = s0 + lane;
-        int nn = 0, base = 0;
-        if (si < nseq) {
-          nn = p.cu_q[si + 1] - p.cu_q[si];
-          base = clamp_len(p.context_lens[si]) - nn;
-        }
-        const bool take = si < nseq && nn >= 2;
-        const uint64_t bal = __ballot(take);
-        const int pos = cnt + __builtin_popcountll(bal & ((1ull << lane) - 1ull));
-        if (take) {
-          sm_base[pos] = base;
-          sm_n[pos] = nn;
-          sm_seq[pos] = si;
-        }
-        cnt += __builtin_popcountll(bal);
+    const int nchunks = (nseq + 63) / 64;
+    // every wave reads its chunks at once (wave w: chunks w, w + NW, ...)
+    constexpr int CPW = (kMaxScheduledSeqs / 64 + NW - 1) / NW;
+    int cb[CPW], cn[CPW], ca[CPW];
+    uint64_t cbal[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int si = (wave + c * NW) * 64 + lane;
+      int nn = 0, base = 0, aa = 0;
+      if (si < nseq) {
+        aa = p.cu_q[si];
+        nn = p.cu_q[si + 1] - aa;
+        base = clamp_len(p.context_lens[si]) - nn;
       }
-      if (lane == 0) *sm_count = cnt;
+      cbal[c] = __ballot(si < nseq && nn >= 2);
+      cb[c] = base;
+      cn[c] = nn;
+      ca[c] = aa;
+    }
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      if (lane == 0 && wave + c * NW < nchunks) sm_cnt[wave + c * NW] = __builtin_popcountll(cbal[c]);
+    __syncthreads();
+    const int mine = lane < nchunks ? sm_cnt[lane] : 0;
+    const int M = min(wave_sum_i32(mine), nseq);
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int ch = wave + c * NW;
+      if (ch < nchunks) {
+        const int off = wave_sum_i32(lane < ch ? mine : 0);
+        const int pos = off + __builtin_popcountll(cbal[c] & ((1ull << lane) - 1ull));
+        if (((cbal[c] >> lane) & 1ull) && pos < kMaxScheduledSeqs) {
+          sm_base[pos] = cb[c];
+          sm_n[pos] = cn[c];
+          sm_a[pos] = ca[c];
+          sm_seq[pos] = ch * 64 + lane;
+        }
+      }
     }
     __syncthreads();
-    const int M = __builtin_amdgcn_readfirstlane(*sm_count);
     const int pair = bx / p.num_kv_heads;
     g = bx % p.num_kv_heads;
-    // number of tiles whose key exceeds K (every wave computes it; the result is wave-uniform)
+    if (M == 0) return;
+    // With at most 64 entries lane m keeps entry m in registers for the search.
+    const int eb = lane < M ? sm_base[lane] : 0, en = lane < M ? sm_n[lane] : 0;
+    auto tiles_gt = [&](int K, int base, int nn) {  // tiles of one sequence whose key exceeds K
+      const int x = K - base;
+      const int T = (nn + TOKW - 1) / TOKW;
+      return x < 0 ? T : (x >= nn ? 0 : T - x / TOKW);
+    };
+    // number of tiles whose key exceeds K (wave-uniform)
     auto count_gt = [&](int K) {
       int c = 0;
-      for (int m = lane; m < M; m += 64) {
-        const int x = K - sm_base[m], nn = sm_n[m];
-        const int T = (nn + TOKW - 1) / TOKW;
-        c += x < 0 ? T : (x >= nn ? 0 : T - x / TOKW);
+      if (M <= 64) {
+        c = tiles_gt(K, eb, en);
+      } else {
+        for (int m = lane; m < M; m += 64) c += tiles_gt(K, sm_base[m], sm_n[m]);
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-      return __builtin_amdgcn_readfirstlane(c);
+      return wave_sum_i32(c);
     };
     int klo = INT_MAX, khi = INT_MIN;
     for (int m = lane; m < M; m += 64) {
       klo = min(klo, sm_base[m] + 1);
       khi = max(khi, sm_base[m] + sm_n[m]);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      klo = min(klo, __shfl_xor(klo, off));
-      khi = max(khi, __shfl_xor(khi, off));
-    }
-    klo = __builtin_amdgcn_readfirstlane(klo);
-    khi = __builtin_amdgcn_readfirstlane(khi);
-    if (M == 0 || pair >= count_gt(klo - 1)) return;  // spare work-group
-    // the key of the unit of rank `pair`: the largest K with more than `pair` keys >= K
-    while (klo < khi) {
-      const int mid = klo + (int)(((long long)khi - klo + 1) / 2);
-      if (count_gt(mid - 1) > pair) klo = mid;
-      else khi = mid - 1;
+    klo = wave_min_i32(klo);
+    khi = wave_max_i32(khi);
+    if (pair >= count_gt(klo - 1)) return;  // spare work-group
+    // the key of the unit of rank `pair`: the largest K with more than `pair` keys >= K (the
+    // count falls as K grows).
+    if (M <= 16) {
+      // 64 probes a round, one per lane, each counting over the entries (read from lane m): the
+      // true probes are a prefix of the lanes, and the answer lies between the last true probe
+      // and the next; a range of 2^18 keys takes three rounds.
+      while (klo < khi) {
+        const long long span = (long long)khi - klo + 1;
+        const int c = klo + (int)((span * lane + 63) / 64);  // lane 0: klo, always true
+        int cnt = 0;
+        for (int m = 0; m < M; ++m)
+          cnt += tiles_gt(c - 1, __builtin_amdgcn_readlane(eb, m), __builtin_amdgcn_readlane(en, m));
+        const uint64_t bal = __ballot(c <= khi && cnt > pair);
+        const int h = 63 - __builtin_clzll(bal | 1ull);
+        const int lo = klo + (int)((span * h + 63) / 64);
+        const int hi = h == 63 ? khi : klo + (int)((span * (h + 1) + 63) / 64) - 1;
+        klo = lo;
+        khi = hi;
+      }
+    } else {
+      while (klo < khi) {
+        const int mid = klo + (int)(((long long)khi - klo + 1) / 2);
+        if (count_gt(mid - 1) > pair) klo = mid;
+        else khi = mid - 1;
+      }
     }
     const int rank_in_key = pair - count_gt(klo);  // among the tiles whose key equals klo
-    s = -1;
-    tile = 0;
-    int seen = 0;
+    int idx = -1, seen = 0;
     for (int m0 = 0; m0 < M; m0 += 64) {
       const int m = m0 + lane;
       bool has = false;
-      int tt = 0;
       if (m < M) {
         const int x = klo - sm_base[m], nn = sm_n[m];
         has = x == nn || (x >= TOKW && x < nn && x % TOKW == 0);
-        tt = x == nn ? (nn + TOKW - 1) / TOKW - 1 : x / TOKW - 1;
       }
       const uint64_t bal = __ballot(has);
       const int c = __builtin_popcountll(bal);
       if (rank_in_key < seen + c) {
         const bool me = has && __builtin_popcountll(bal & ((1ull << lane) - 1ull)) == rank_in_key - seen;
-        const int src = __builtin_ctzll(__ballot(me));
-        s = __shfl(m < M ? sm_seq[m] : 0, src);
-        tile = __shfl(tt, src);
+        idx = m0 + __builtin_ctzll(__ballot(me));
         break;
       }
       seen += c;
     }
     // wave-uniform from here on (every lane took the same branch of the search)
-    s = __builtin_amdgcn_readfirstlane(s);
-    tile = __builtin_amdgcn_readfirstlane(tile);
-    if (s < 0) return;  // not reached: every rank below the unit count has a unit
-    __syncthreads();    // the schedule's arrays are done with before the tiles reuse them
+    idx = __builtin_amdgcn_readfirstlane(idx);
+    if (idx < 0) return;  // not reached: every rank below the unit count has a unit
+    s = __builtin_amdgcn_readfirstlane(sm_seq[idx]);
+    a = __builtin_amdgcn_readfirstlane(sm_a[idx]);
+    n = __builtin_amdgcn_readfirstlane(sm_n[idx]);
+    L = __builtin_amdgcn_readfirstlane(sm_base[idx]) + n;
+    const int x = klo - (L - n);
+    tile = x == n ? (n + TOKW - 1) / TOKW - 1 : x / TOKW - 1;
+    __syncthreads();  // the schedule's arrays are done with before the tiles reuse them
+    if (s < 0 || s >= nseq || tile < 0) return;  // not reached: the search lands on a compacted entry
   } else {
     // natural order, the last query tiles of a chunk (the most keys) first
     g = bx;
     tile = grid_y - 1 - by;
     s = bz;
+    a = load_invariant(p.cu_q + s);
+    n = load_invariant(p.cu_q + s + 1) - a;
+    L = clamp_len(load_invariant(p.context_lens + s));
   }
 
-  const int a = load_invariant(p.cu_q + s);
-  const int n = load_invariant(p.cu_q + s + 1) - a;
   if (n <= 1) return;  // decode rows: the decode kernel
   const int i0 = tile * TOKW;
   if (i0 >= n) return;
-  const int L = clamp_len(load_invariant(p.context_lens + s));
   const bool causal = p.causal != 0;
   // keys any row of this work-group may see
   const int last_tok = min(n, i0 + TOKW) - 1;
@@ -227,14 +270,13 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
     const int h = r % G;
     const bool ok = tok[j] < n;
     lim[j] = ok ? (causal ? min(L, L - n + tok[j] + 1) : L) : 0;  // keys [0, lim) visible
+    // A row past the chunk reads the chunk's first row instead: its scores are finite, and its
+    // weights never reach an output (every key is masked for it where masking applies, and its
+    // row is not stored).  Nothing here waits for the loads.
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(p.query) + ((size_t)(a + (ok ? tok[j] : 0)) * hq + (size_t)g * G + h) * D;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg);
-      if constexpr (E8) v = bf16x8_to_f16(v);
-      qb[j][kk] = ok ? v : make_uint4(0, 0, 0, 0);
-    }
+    for (int kk = 0; kk < KS; ++kk) qb[j][kk] = *reinterpret_cast<const uint4*>(qrow + 32 * kk + 8 * lg);
   }
 
   float m_run[NT];
@@ -272,6 +314,7 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
   };
 
   const int ntiles = (kv_end + KT - 1) / KT;
+
   // Tile kt+1 is fetched into registers while tile kt is multiplied; K and V chunks are taken
   // in row order (coalesced loads, one 16-byte LDS store each).
   raw_t kreg[LOADS], vreg[LOADS];
@@ -326,9 +369,9 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
     chunk_ok = okm;
     tile_whole = __builtin_amdgcn_readfirstlane(all_valid ? 1 : 0);
   };
-  // Tile kt is multiplied out of buffer kt % 2 while tile kt + 1 waits in registers; after
-  // the multiply it goes to the other buffer (free since the previous barrier) and the loads
-  // of tile kt + 2 are issued: one barrier per tile.
+  // Tile i is multiplied out of buffer i % 2 while tile i + 1 waits in registers;
+  // after the multiply it goes to the other buffer (free since the previous barrier) and the loads
+  // of tile i + 2 are issued: one barrier per tile.
   auto store = [&](int buf) {
     uint16_t* kd = lds + buf * KBUF;
     uint16_t* vd = lds + 2 * KBUF + buf * VBUF;
@@ -351,38 +394,47 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
       *reinterpret_cast<uint4*>(vd + key * VP + c * 8) = ok ? widen(vreg[u]) : make_uint4(0, 0, 0, 0);
     }
   };
-  // Pipeline: at the top of iteration kt, tile kt+1 (loaded during iteration kt-1) goes to the idle
-  // LDS buffer and the loads of tile kt+2 are issued; tile kt is multiplied out of the other buffer;
-  // one barrier ends the iteration.  The loads then have a whole tile's products to land.
-  // The query operands are ready before the tile loop (their loads waited for here, once).
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qb[j][kk].x), "+v"(qb[j][kk].y), "+v"(qb[j][kk].z), "+v"(qb[j][kk].w));
+  // Pipeline: at the top of step i, tile i+1 (loaded during step i-1) goes to the idle LDS buffer
+  // and the loads of tile i+2 are issued; tile i is multiplied out of the other buffer; one barrier
+  // ends the step.  The loads then have a whole tile's products to land.  The table reads and K/V
+  // loads of the first tiles are issued while the query rows are still in flight.
   TileBlocks tb_next{};
   if (ntiles > 0) {
     fetch(0, read_table(0));
     if (ntiles > 1) tb_next = read_table(1);
     store(0);
-    lds_barrier();
-    if (ntiles > 1) {
-      fetch(1, tb_next);
-      if (ntiles > 2) tb_next = read_table(2);
-    }
   }
-  // One tile step; MASKED = false for the tiles that every row of the work-group sees whole (no
-  // key past any row's visible range), so their code holds no masking at all.
-  auto tile_step = [&](int kt, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if (kt + 1 < ntiles) {
-      store((kt + 1) & 1);
-      if (kt + 2 < ntiles) {
-        fetch(kt + 2, tb_next);
-        if (kt + 3 < ntiles) tb_next = read_table(kt + 3);
+  lds_barrier();
+  if (ntiles > 1) {
+    fetch(1, tb_next);
+    if (ntiles > 2) tb_next = read_table(2);
+  }
+  // The query operands are ready before the tile loop (their loads waited for here, once, after
+  // the first tiles' loads are on their way; over an E5M2 cache they are taken to f16 here).
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if constexpr (E8) qb[j][kk] = bf16x8_to_f16(qb[j][kk]);
+      asm volatile("" : "+v"(qb[j][kk].x), "+v"(qb[j][kk].y), "+v"(qb[j][kk].z), "+v"(qb[j][kk].w));
+    }
+  // Tile i + 1 from registers to its LDS buffers and the loads of tile i + 2 issued.
+  auto advance = [&](int i) {
+    if (i + 1 < ntiles) {
+      store((i + 1) & 1);
+      if (i + 2 < ntiles) {
+        fetch(i + 2, tb_next);
+        if (i + 3 < ntiles) tb_next = read_table(i + 3);
       }
     }
-    const uint16_t* Ks = lds + (kt & 1) * KBUF;
-    const uint16_t* Vs = lds + 2 * KBUF + (kt & 1) * VBUF;
+  };
+  // Scores and weights of tile i (P, in the B-operand key order); MASKED = false for the tiles
+  // that every row of the work-group sees whole (no key past any row's visible range), so their
+  // code holds no masking at all.
+  auto scores = [&](int i, auto masked_tag, uint4 (&pb)[NT][2]) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int kt = i;
+    const uint16_t* Ks = lds + (i & 1) * KBUF;
     // ---- S^T = K Q^T for the tile's 4 groups of 16 keys ------------------------------------
     // k-step outermost: 4*NT independent accumulators between dependent MFMAs
     f32x4_t sacc[NT][4];
@@ -403,23 +455,22 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
     // ---- mask, online softmax (threshold rescale), P in the B-operand key order -----------
     // Masking is needed only where a row's visible range ends inside the tile.
     const bool whole = !MASKED || __builtin_amdgcn_readfirstlane(kt * KT + KT <= wave_lim_min ? 1 : 0) != 0;
-    uint4 pb[NT][2];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       if (!whole) {  // the scores in place, so both cases share the code that follows
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt * KT + m * 16 + 4 * lg + i;
-            sacc[j][m][i] = key < lim[j] ? sacc[j][m][i] : -__builtin_inff();
+          for (int e = 0; e < 4; ++e) {
+            const int key = kt * KT + m * 16 + 4 * lg + e;
+            sacc[j][m][e] = key < lim[j] ? sacc[j][m][e] : -__builtin_inff();
           }
       }
       float mx = -__builtin_inff();
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[j][m][i]);
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[j][m][e]);
       // The row's running max only moves when some score exceeds it by more than the
       // threshold; the lanes' own maxima decide whether the row maxima are needed at all.
       if (__any(mx * p.scale_log2 > m_run[j] + kTauPrefill)) {  // scale > 0
@@ -442,7 +493,7 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
         typedef std::conditional_t<E8, _Float16, __bf16> pel_t;
         pel_t b[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = (pel_t)fast_exp2(fmaf(sacc[j][m][i], p.scale_log2, mneg));  // -inf -> 0
+        for (int e = 0; e < 4; ++e) b[e] = (pel_t)fast_exp2(fmaf(sacc[j][m][e], p.scale_log2, mneg));  // -inf -> 0
         pk[m][0] = (uint32_t)__builtin_bit_cast(uint16_t, b[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, b[1]) << 16);
         pk[m][1] = (uint32_t)__builtin_bit_cast(uint16_t, b[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, b[3]) << 16);
       }
@@ -452,8 +503,10 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
       lacc[j] = mfma_16x16x32<E8>(kOnes, pb[j][0], lacc[j]);
       lacc[j] = mfma_16x16x32<E8>(kOnes, pb[j][1], lacc[j]);
     }
-
-    // ---- O^T += V^T P^T --------------------------------------------------------------------
+  };
+  // O^T += V^T P^T for the tile in V buffer vb.
+  auto accumulate = [&](int vb, const uint4 (&pb)[NT][2]) {
+    const uint16_t* Vs = lds + 2 * KBUF + vb * VBUF;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -466,14 +519,21 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
         for (int j = 0; j < NT; ++j) oacc[j][dt] = mfma_16x16x32<E8>(va, pb[j][ks], oacc[j][dt]);
       }
     }
-    lds_barrier();
   };
   // tiles below the smallest visible range of the work-group's rows (its first token's) are whole
   const int wg_lim_min = causal ? min(L, L - n + i0 + 1) : L;
   const int kt_whole = __builtin_amdgcn_readfirstlane(min(ntiles, max(0, wg_lim_min) / KT));
-  int kt = 0;
-  for (; kt < kt_whole; ++kt) tile_step(kt, std::false_type{});
-  for (; kt < ntiles; ++kt) tile_step(kt, std::true_type{});
+  // step i: tile i's scores, weights and values, then the barrier
+  auto step = [&](int i, auto masked_tag) {
+    advance(i);
+    uint4 pb[NT][2];
+    scores(i, masked_tag, pb);
+    accumulate(i & 1, pb);
+    lds_barrier();
+  };
+  int i = 0;
+  for (; i < kt_whole; ++i) step(i, std::false_type{});
+  for (; i < ntiles; ++i) step(i, std::true_type{});
 
   // ---- normalise and store: lane l holds dims dt*16 + 4*lg .. +3 of row l%16 --------------
 #pragma unroll
@@ -485,8 +545,8 @@ __device__ __forceinline__ void prefill_body(const DecodeParams& p, int bx, int 
     uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(a + tok[j]) * hq + (size_t)g * G + r % G) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint32_t w0 = f32_to_bf16_rne(oacc[j][dt][0] * inv) | (f32_to_bf16_rne(oacc[j][dt][1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16_rne(oacc[j][dt][2] * inv) | (f32_to_bf16_rne(oacc[j][dt][3] * inv) << 16);
+      const uint32_t w0 = pack_bf16x2(oacc[j][dt][0] * inv, oacc[j][dt][1] * inv);
+      const uint32_t w1 = pack_bf16x2(oacc[j][dt][2] * inv, oacc[j][dt][3] * inv);
       *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * lg) = make_uint2(w0, w1);
     }
   }
