@@ -10,6 +10,12 @@
 // in dispatch order, each list longest first.  A CU then holds work-groups of both roles at once:
 // while one waits on HBM the other keeps the matrix cores busy.
 //
+// Work-group i runs on XCD i % 8 (round-robin dispatch), and every XCD has its own L2.  The query
+// tiles of one (sequence, KV head) re-read the same K/V tiles, so the interleave is made within
+// each residue class of the dispatch index mod 8, and the unit of rank r goes to class r % 8: with
+// up to 8 KV heads (or a multiple of 8) every unit of a head runs on the same XCD and finds its
+// tiles in that XCD's L2.
+//
 // The decode role runs only whole-context passes (no split-KV partitions; the caller's launch
 // falls back to the two kernels otherwise).
 #include "decode_body.hpp"
@@ -59,18 +65,22 @@ template <int D, int G, bool E8>
 __global__ __launch_bounds__(256, 2) void packed_step_kernel(const DecodeParams p, int n_pre_bound, int n_dec) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[PackedSmem<D, G>::BYTES];
   // The roles are interleaved over the prefill work-groups the batch needs, not the host's bound;
-  // the grid's surplus (the bound minus that count) sits at the end and returns at once.
+  // each class's surplus positions come last in it and return at once.
   const int n_pre =
       min(n_pre_bound, packed_prefill_units<128 / G>(p, n_dec / p.num_kv_heads, reinterpret_cast<int*>(smem)));
-  if ((int)blockIdx.x >= n_pre + n_dec) return;
-  const int2 r = packed_role(blockIdx.x, n_pre, n_pre + n_dec);
+  const int x = (int)blockIdx.x & 7, q = (int)blockIdx.x >> 3;  // class and position in it
+  const int npx = n_pre > x ? (n_pre - x + 7) >> 3 : 0;          // ranks x, x + 8, ... of each list
+  const int ndx = n_dec > x ? (n_dec - x + 7) >> 3 : 0;
+  if (q >= npx + ndx) return;
+  const int2 r = packed_role(q, npx, npx + ndx);
+  const int rank = r.y * 8 + x;
   if (r.x) {
-    prefill_body<D, G, E8>(p, r.y, 0, 0, 1, reinterpret_cast<uint16_t*>(smem));
+    prefill_body<D, G, E8>(p, rank, 0, 0, 1, reinterpret_cast<uint16_t*>(smem));
   } else {
     constexpr int KV = E8 ? KV_E5M2 : KV_BF16;
     int* sm_i = reinterpret_cast<int*>(smem);
     float* sm_f = reinterpret_cast<float*>(smem + 4 * DecodeSmem<G, D, 4>::INTS);
-    decode_body<KV, D, G, 4>(p, r.y % p.num_kv_heads, 0, r.y / p.num_kv_heads, p.num_kv_heads,
+    decode_body<KV, D, G, 4>(p, rank % p.num_kv_heads, 0, rank / p.num_kv_heads, p.num_kv_heads,
                              n_dec / p.num_kv_heads, sm_i, sm_f);
   }
 }
@@ -87,13 +97,15 @@ static hipError_t launch_packed_dg(const DecodeParams& p, int num_seqs, int tota
   const long long units = std::min<long long>((total_q + chunks * (TOKW - 1)) / TOKW, tiles_per_seq * num_seqs);
   const long long n_pre = units * p.num_kv_heads;
   const long long n_dec = (long long)num_seqs * p.num_kv_heads;
-  if (n_pre + n_dec > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  // eight classes of ceil(n_pre / 8) + ceil(n_dec / 8) positions
+  const long long grid = 8 * ((n_pre + 7) / 8 + (n_dec + 7) / 8);
+  if (grid > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   q.sched_seqs = num_seqs;
   q.longest_first = 1;
   q.snake = 0;
   q.resident = 0;
-  hipLaunchKernelGGL((packed_step_kernel<D, G, E8>), dim3((unsigned)(n_pre + n_dec)), dim3(256), 0, stream, q,
-                     (int)n_pre, (int)n_dec);
+  hipLaunchKernelGGL((packed_step_kernel<D, G, E8>), dim3((unsigned)grid), dim3(256), 0, stream, q, (int)n_pre,
+                     (int)n_dec);
   return hipGetLastError();
 }
 
