@@ -3,7 +3,9 @@
 The decode and prefill kernels each turn a work-group index into a work unit with integer
 steps that every work-group repeats on its own (decode: rank the sequences by length, take the
 unit of its rank, mirror every second lap when the grid is resident; prefill: count the query
-tiles above a key, binary-search the key of its rank, resolve ties by sequence).  The GPU parity
+tiles above a key, search the key of its rank -- 64 probes a round, one per lane, with up to 16
+prefill sequences, else bisection -- and resolve ties by sequence; packed step: interleave the
+two roles within each residue class of the work-group index mod 8).  The GPU parity
 tests show that every output row gets computed; these tests replay the same integer steps in
 Python on many random batches and check the properties the order is meant to have: the grid maps
 onto the units one to one, in the intended order, and the host's grid bound covers every unit.
@@ -108,12 +110,21 @@ def prefill_schedule(cu_q, context_lens, tokw):
         if pair >= count_gt(klo - 1):
             out.append(None)
             continue
-        while klo < khi:
-            mid = klo + (khi - klo + 1) // 2
-            if count_gt(mid - 1) > pair:
-                klo = mid
-            else:
-                khi = mid - 1
+        if len(comp) <= 16:
+            while klo < khi:  # lane l probes klo + ceil(span * l / 64); the true lanes are a prefix
+                span = khi - klo + 1
+                probes = [klo + (span * lane + 63) // 64 for lane in range(64)]
+                true = [c <= khi and count_gt(c - 1) > pair for c in probes]
+                h = max(lane for lane in range(64) if true[lane])
+                assert all(true[:h + 1]) and not any(true[h + 1:])
+                klo, khi = probes[h], (khi if h == 63 else probes[h + 1] - 1)
+        else:
+            while klo < khi:
+                mid = klo + (khi - klo + 1) // 2
+                if count_gt(mid - 1) > pair:
+                    klo = mid
+                else:
+                    khi = mid - 1
         rank_in_key = pair - count_gt(klo)
         seen = 0
         unit = None
@@ -164,3 +175,56 @@ def test_prefill_order_is_a_bijection_in_descending_key(G, seed):
     for s, t, k in units:  # the key is the keys seen by the tile's last row
         base = int(lens[s] - q[s])
         assert k == base + min(int(q[s]), (t + 1) * tokw)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_order_over_wide_key_ranges(seed):
+    # contexts far apart (tens of thousands of keys) and few chunks: the lane-probe search takes
+    # several rounds
+    rng = np.random.default_rng(500 + seed)
+    nseq = int(rng.integers(2, 10))
+    q = rng.integers(2, 700, size=nseq)
+    lens = rng.integers(0, 60000, size=nseq) + q
+    cu = np.concatenate([[0], np.cumsum(q)]).astype(np.int64)
+    got, _ = prefill_schedule(cu, lens, 32)
+    keys = [k for u in got if u is not None for k in [u[2]]]
+    assert keys == sorted(keys, reverse=True)
+    assert sorted((s, t) for s, t, _ in (u for u in got if u is not None)) == sorted(
+        (s, t) for s in range(nseq) for t in range((q[s] + 31) // 32))
+
+
+# ---------------------------------------------------------------- packed step: roles per XCD class
+def packed_positions(n_pre, n_dec):
+    """(role, rank) of every position of the packed-step grid, or None for a spare position: the
+    roles are interleaved evenly within each residue class of the position mod 8, and class x takes
+    the ranks x, x + 8, ... of both lists."""
+    grid = 8 * ((n_pre + 7) // 8 + (n_dec + 7) // 8)
+    out = []
+    for b in range(grid):
+        x, q = b % 8, b // 8
+        npx = (n_pre - x + 7) // 8 if n_pre > x else 0
+        ndx = (n_dec - x + 7) // 8 if n_dec > x else 0
+        if q >= npx + ndx:
+            out.append(None)
+            continue
+        before, upto = q * npx // (npx + ndx), (q + 1) * npx // (npx + ndx)
+        role, idx = (1, before) if upto > before else (0, q - before)
+        out.append((role, idx * 8 + x))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_packed_roles_cover_both_lists_on_their_xcd(seed):
+    rng = np.random.default_rng(900 + seed)
+    for _ in range(50):
+        n_pre, n_dec = int(rng.integers(0, 2000)), int(rng.integers(0, 2000))
+        pos = packed_positions(n_pre, n_dec)
+        taken = [p for p in pos if p is not None]
+        assert sorted(r for role, r in taken if role == 1) == list(range(n_pre))
+        assert sorted(r for role, r in taken if role == 0) == list(range(n_dec))
+        assert all(p is None or p[1] % 8 == b % 8 for b, p in enumerate(pos))  # rank's class = XCD
+        for x in range(8):  # within a class both lists keep their order (longest first)
+            cls = [p for p in pos[x::8] if p is not None]
+            for role in (0, 1):
+                ranks = [r for ro, r in cls if ro == role]
+                assert ranks == sorted(ranks)
