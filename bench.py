@@ -202,7 +202,7 @@ class VarlenBatch:
         self.args_write = (P(self.knew), P(self.vnew), P(self.pk), P(self.pv), P(self.slots), self.ntok, hkv, d, bs,
                            nb, bf, kd)
 
-        def varlen_args(s0, s1):
+        def varlen_args(s0, s1, part):
             rows0 = int(w.cu_seqlens_q[s0])
             cu = torch.from_numpy((w.cu_seqlens_q[s0 : s1 + 1] - rows0).astype("int32")).to(dev)
             self._keep.append(cu)
@@ -210,12 +210,13 @@ class VarlenBatch:
             qoff = rows0 * w.num_q_heads * d * 2
             return (P(self.out) + qoff, P(self.q) + qoff, P(self.pk), P(self.pv), P(cu), P(self.lens) + 4 * s0,
                     P(self.tables) + 4 * mb * s0, mb, s1 - s0, int(w.q_lens[s0:s1].sum()), qlen, hkv, g, d, bs, nb,
-                    ml, w.scale, 1, bf, kd, partition, P(self.ws), self.ws.numel())
+                    ml, w.scale, 1, bf, kd, part, P(self.ws), self.ws.numel())
 
         self._keep = []
-        self.args_varlen = varlen_args(0, n)
-        self.args_prefill_only = varlen_args(0, n_pre) if n_pre > 0 else None
-        self.args_decode_only = varlen_args(n_pre, n) if n_pre < n else None
+        self.args_varlen = varlen_args(0, n, partition)
+        # the sub-batches run with the full batch's partition size, as its rows do in the full step
+        self.args_prefill_only = varlen_args(0, n_pre, self.resolved) if n_pre > 0 else None
+        self.args_decode_only = varlen_args(n_pre, n, self.resolved) if n_pre < n else None
         self.kv_bytes = int(w.context_lens.astype("int64").sum()) * hkv * 2 * row_bytes(w)
         self.decode_kv_bytes = int(w.context_lens[n_pre:].astype("int64").sum()) * hkv * 2 * row_bytes(w)
         pos = [(int(L) - int(qn) + i + 1) for L, qn in zip(w.context_lens[:n_pre], w.q_lens[:n_pre]) for i in range(qn)]
@@ -299,8 +300,8 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
             "block_size": w0.block_size,
             "partition_tokens": batches[0].resolved,
             "resident_batches": reps,
-            "step": "slot mapping + cache write of every new token + paged_attention_varlen "
-                    "(decode rows on the decode kernel, prefill rows on MFMA tiles)",
+            "step": "slot mapping + cache write of every new token + paged_attention_varlen (one launch of "
+                    "the two-role packed-step kernel: decode rows streamed, prefill tiles on MFMA)",
         },
         "seq_steps_per_s": round(w0.num_seqs / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -312,13 +313,14 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config]),
+            "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config], [i % reps for i in range(args.steps)]),
             "avg_launch_us": round(dec_ms * 1e3, 3),
             "launch_distribution": launch_stats(dec_list),
             "algorithmic_bytes_per_launch": int(dec_bytes),
         },
         "prefill_mfma": {
-            "kernel": "varlen_prefill_kernel (prefill rows alone; the call also issues an empty decode launch)",
+            "kernel": "prefill rows alone, launched as in the full step: one packed-step launch whose decode "
+                      "work-groups find no 1-token row and return",
             "bound": "mfma",
             "achieved": round(pre_tflops, 2),
             "peak": 2500.0,
@@ -384,7 +386,7 @@ def bench_multi_token(args, batches, timed, call, step, np):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(call_gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config]),
+            "traffic": measured_traffic(args.traffic, CONFIG_NAMES[args.config], [i % reps for i in range(args.steps)]),
             "avg_launch_us": round(call_ms * 1e3, 3),
             "launch_distribution": launch_stats(call_list),
             "algorithmic_bytes_per_launch": int(step_bytes),
@@ -505,7 +507,7 @@ def main():
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     kern_gbs = step_bytes / (kern_avg * 1e-3) / 1e9
 
-    traffic = measured_traffic(args.traffic, CONFIG_NAMES[args.config])
+    traffic = measured_traffic(args.traffic, CONFIG_NAMES[args.config], [i % reps for i in range(args.steps)])
 
     cpu = args.cpu_result
 
@@ -569,7 +571,7 @@ def main():
 # Sources each measured kernel is built and launched from: its traffic figure only counts while
 # they are unchanged.
 KERNEL_SOURCES = {
-    "decode": ("decode.hip", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
+    "decode": ("decode.hip", "decode_body.hpp", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
     "multiquery": ("multiquery.hip", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
 }
 
@@ -591,9 +593,11 @@ def kernel_source_digest(family: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(path, workload):
+def measured_traffic(path, workload, replicas=None):
     """HBM bytes per launch of the dominant kernel for this workload, from the committed
-    rocprofv3 counter summary, or None when it is missing or was taken on other sources."""
+    rocprofv3 counter summary, or None when it is missing or was taken on other sources.  The
+    summary holds the bytes of each resident batch (they differ in size); `replicas` lists the
+    batch of every timed step, and the result is their mean, like the algorithmic bytes."""
     if not path or not os.path.exists(path):
         return None
     with open(path) as f:
@@ -601,6 +605,9 @@ def measured_traffic(path, workload):
     entry = rec.get("workloads", {}).get(workload)
     if entry is None or entry.get("source_sha256") != kernel_source_digest(kernel_family(workload)):
         return None
+    by_rep = entry.get("hbm_bytes_by_replica")
+    if replicas and by_rep and all(0 <= r < len(by_rep) and by_rep[r] for r in replicas):
+        return int(round(sum(by_rep[r] for r in replicas) / len(replicas)))
     return entry.get("hbm_bytes_per_launch")
 
 
