@@ -550,7 +550,7 @@ def main():
                      (" + separate reduce kernel" if batches[0].split else "")},
         "wall_s": round(wall, 4),
         "roofline": {
-            "kernel": "decode_partition_kernel" + (" (append mode" if fused else " (") + f", {w0.kv_dtype.upper()} pool)",
+            "kernel": decode_kernel_name(w0) + (" (append mode" if fused else " (") + f", {w0.kv_dtype.upper()} pool)",
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -568,10 +568,16 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+def decode_kernel_name(w) -> str:
+    """The partition kernel a decode call launches: groups of 8 or 16 query heads per KV head over
+    a bf16 or E5M2 cache run on MFMA, every other shape on the vector kernel."""
+    return "decode_mfma_kernel" if w.gqa_group in (8, 16) and w.kv_dtype in ("bf16", "e5m2") else "decode_partition_kernel"
+
+
 # Sources each measured kernel is built and launched from: its traffic figure only counts while
 # they are unchanged.
 KERNEL_SOURCES = {
-    "decode": ("decode.hip", "decode_body.hpp", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
+    "decode": ("decode.hip", "decode_body.hpp", "multiquery.hip", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
     "multiquery": ("multiquery.hip", "pa_device.hpp", "pa_launch.hpp", "api.cpp"),
 }
 

@@ -133,6 +133,14 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p
 // its four rows is the whole flush (no LDS merge across waves, no barrier), and a CU holds a
 // dozen partitions at once; measured on 8 contexts of 32768 tokens in 512-token partitions, 3 to
 // 4 % faster than four waves per partition.
+// Groups of 8 or 16 query heads per KV head over a bf16 or E5M2 cache take the partition pass on
+// MFMA (multiquery.hip).  With G = 8 the vector kernel spends twice the FMAs per KV byte of G = 4
+// and falls behind the memory.  Measured on the fused decode step: 64 sequences of 512..2048
+// tokens with 64 query / 8 KV heads 63.8 us against 69.5 us; 8 x 32768 tokens in 512-token
+// partitions 187.5 us against 205.5 us for the partition launch.
+#ifndef PA_DECODE_MFMA_WIDE_GROUPS
+#define PA_DECODE_MFMA_WIDE_GROUPS 1
+#endif
 #ifndef PA_DECODE_WAVES_WHOLE
 #define PA_DECODE_WAVES_WHOLE 4
 #endif
@@ -214,6 +222,8 @@ static hipError_t launch_parts_kv_d(const DecodeParams& p, int gqa, int num_seqs
 
 hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
                                     hipStream_t stream) {
+  if (PA_DECODE_MFMA_WIDE_GROUPS && decode_mfma_applies(p, kv_kind, head_dim, gqa))
+    return launch_decode_mfma(p, kv_kind, head_dim, gqa, num_seqs, stream);
   if (head_dim == 128) {
     if (kv_kind == KV_F32) return launch_parts_kv_d<KV_F32, 128>(p, gqa, num_seqs, stream);
     if (kv_kind == KV_BF16) return launch_parts_kv_d<KV_BF16, 128>(p, gqa, num_seqs, stream);

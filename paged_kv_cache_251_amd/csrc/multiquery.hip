@@ -19,6 +19,15 @@
 //                                          the wave's own row-major copy of the block in LDS with
 //                                          ds_read_b64_tr_b16
 // Row sums come from the same rounded weights through an MFMA with a ones matrix.
+//
+// The same body serves the decode calls when a KV head is shared by 8 or more query heads (DEC):
+// one query row per sequence, whose G heads are the rows of the tile, over the decode grid
+// (KV head, partition, sequence).  There the vector-ALU decode kernel spends two f32 FMAs per
+// head per element; the matrix cores take the products, and only the widening and the softmax are
+// left to the vector ALU.  A split partition writes its rows' (o/l, m, l) to the decode workspace
+// for the reduce kernel, and the append of the newest token is done here as in the vector kernel:
+// the work-group whose range holds position L-1 stores the new rows (cast to E5M2 for that cache)
+// and uses the same cast values for that token instead of reading its slot back.
 #include <atomic>
 #include <type_traits>
 
@@ -65,12 +74,16 @@ __device__ __forceinline__ uint2 mq_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p)));
 }
 
+__device__ __forceinline__ const int32_t* table_of(const DecodeParams& p, int s) {
+  return p.block_tables + (size_t)s * p.max_blocks_per_seq;
+}
+
 }  // namespace
 
 // E8: the cache holds E5M2 codes, widened to f16 as they are loaded; queries and probabilities
-// in f16 and the products on the f16 MFMA.
-template <int D, int G, int NT, bool E8>
-__global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeParams p) {
+// in f16 and the products on the f16 MFMA.  DEC: the decode calls (see above).
+template <int D, int G, int NT, bool E8, bool DEC>
+__device__ __forceinline__ void mq_body(const DecodeParams& p) {
   constexpr int W = 4;
   constexpr int ROWS = NT * 16;       // query rows of the work-group: row r = (token r / G, head r % G)
   constexpr int KS = D / 32;          // k-steps of the QK product
@@ -90,20 +103,35 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
   const int hq = p.num_kv_heads * G;
 
   int s = blockIdx.z, g = blockIdx.x;
+  const int part = DEC ? blockIdx.y : 0;
   if (p.longest_first) {
     int* len = reinterpret_cast<int*>(lds + W * VWAVE * 2);
     const int2 u = longest_first_unit<64 * W>(p.context_lens, gridDim.z, gridDim.x, p.snake, len, len + kMaxRankedMq);
     s = u.x;
     g = u.y;
   }
-  const int a = load_invariant(p.cu_q + s);
-  const int n = load_invariant(p.cu_q + s + 1) - a;
-  if (n <= 1) return;  // single rows: the decode kernel
+  int a, n;
+  if constexpr (DEC) {
+    a = s;  // the sequence's one query row
+    n = 1;
+  } else {
+    a = load_invariant(p.cu_q + s);
+    n = load_invariant(p.cu_q + s + 1) - a;
+    if (n <= 1) return;  // single rows: the decode kernel
+  }
   int L = load_invariant(p.context_lens + s);
   L = L < 0 ? 0 : L;
   L = L > p.max_context_len ? p.max_context_len : L;
   L = L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
-  const bool causal = p.causal != 0;
+  const bool causal = DEC || p.causal != 0;
+  // keys [t0, t1) of this work-group: a decode partition, else the whole context
+  int t0 = 0, t1 = L, nparts = 1;
+  if (DEC && p.partition_tokens > 0) {
+    t0 = part * p.partition_tokens;
+    t1 = min(L, t0 + p.partition_tokens);
+    nparts = (L + p.partition_tokens - 1) / p.partition_tokens;
+    if (part > 0 && t0 >= L) return;
+  }
 
   // ---- query rows (B operand of S^T = K Q^T) ----------------------------------------------
   int tok[NT], lim[NT];
@@ -113,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
     const int r = j * 16 + lr;
     tok[j] = r / G;
     const bool ok = tok[j] < n;
-    lim[j] = ok ? (causal ? min(L, L - n + tok[j] + 1) : L) : 0;  // keys [0, lim) visible
+    lim[j] = ok ? min(t1, causal ? min(L, L - n + tok[j] + 1) : L) : 0;  // keys [0, lim) visible
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(p.query) + ((size_t)(a + (ok ? tok[j] : 0)) * hq + (size_t)g * G + r % G) * D;
 #pragma unroll
@@ -127,8 +155,8 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
   }
   // the keys every valid row of the work-group sees: blocks below need no mask
   const int last_tok = min(n, ROWS / G) - 1;
-  const int lim_min = causal ? min(L, L - n + 1) : L;  // token 0
-  const int kv_end = max(0, causal ? min(L, L - n + last_tok + 1) : L);
+  const int lim_min = min(t1, causal ? min(L, L - n + 1) : L);  // token 0
+  const int kv_end = max(0, min(t1, causal ? min(L, L - n + last_tok + 1) : L));
 
   float m_run[NT];
   mq_f32x4_t lacc[NT], oacc[NT][DT];
@@ -160,12 +188,46 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
   // lane m of group lg reads key 4 lg + m / 4, dims dt * 16 + 4 (m % 4): V^T for dims dt*16 + lr
   const int v_rd = (4 * lg + (lr >> 2)) * VP + 4 * (lr & 3);
 
+  // ---- the newest token (DEC with key_new): its rows in this lane's K and V layouts -------
+  const bool appending = DEC && p.key_new != nullptr && L - 1 >= t0 && L - 1 < t1;
+  const int b_new = appending ? (L - 1) / 16 : -1;
+  const int r_new = (L - 1) & 15;
+  // 8 bf16 as the cache holds them (bf16, or the E5M2 cast widened to f16: a code is the upper
+  // byte of the f16 of the same value)
+  auto cast8 = [](uint4 v) {
+    if constexpr (E8) {
+      auto c = [](uint32_t w) { return (bf16_to_e5m2(w & 0xFFFFu) << 8) | (bf16_to_e5m2(w >> 16) << 24); };
+      return make_uint4(c(v.x), c(v.y), c(v.z), c(v.w));
+    } else {
+      return v;
+    }
+  };
+  const uint16_t* kr = reinterpret_cast<const uint16_t*>(p.key_new) + ((size_t)s * p.num_kv_heads + g) * D;
+  const uint16_t* vr = reinterpret_cast<const uint16_t*>(p.value_new) + ((size_t)s * p.num_kv_heads + g) * D;
+  if (appending) {
+    // the slot, written by wave 0 in the cache's format (nothing in this launch reads it back)
+    const int phys = load_invariant(table_of(p, s) + b_new);
+    if (wave == 0 && lane < CH && phys >= 0 && phys < p.num_blocks) {
+      const size_t el = (((size_t)phys * p.num_kv_heads + g) * 16 + r_new) * D + lane * 8;
+      const uint4 kv = cast8(*reinterpret_cast<const uint4*>(kr + lane * 8));
+      const uint4 vv = cast8(*reinterpret_cast<const uint4*>(vr + lane * 8));
+      if constexpr (E8) {
+        auto pk = [](uint32_t lo, uint32_t hi) { return (lo >> 8 & 0xFFu) | (lo >> 16 & 0xFF00u) | (hi << 8 & 0xFF0000u) | (hi & 0xFF000000u); };
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.key_cache_w) + el) = make_uint2(pk(kv.x, kv.y), pk(kv.z, kv.w));
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(p.value_cache_w) + el) = make_uint2(pk(vv.x, vv.y), pk(vv.z, vv.w));
+      } else {
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.key_cache_w) + el) = kv;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.value_cache_w) + el) = vv;
+      }
+    }
+  }
+
   struct Block {
     uint4 k[KS];
     uint4 v[VLD];
     bool ok;
   };
-  auto load_block = [&](int b, Block& t) {
+  auto load_block = [&](int b, Block& t) __attribute__((always_inline)) {
     int phys = load_invariant(table + b);
     t.ok = phys >= 0 && phys < p.num_blocks;
     phys = t.ok ? phys : 0;
@@ -191,9 +253,20 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
 #pragma unroll
     for (int u = 0; u < VLD; ++u) t.v[u] = ld16(vb + v_off[u], std::true_type{});
     __builtin_amdgcn_sched_barrier(0);  // issue the block before the math that follows
+    if (b == b_new) {  // the appended token: its rows, not the slot being written
+      // read here, not held in registers across the stream (a select between two arrays of
+      // rows would put both in scratch)
+      if (lr == r_new) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) t.k[kk] = cast8(*reinterpret_cast<const uint4*>(kr + 32 * kk + 8 * lg));
+      }
+#pragma unroll
+      for (int u = 0; u < VLD; ++u)
+        if ((lane + 64 * u) / CH == r_new) t.v[u] = cast8(*reinterpret_cast<const uint4*>(vr + ((lane + 64 * u) % CH) * 8));
+    }
   };
 
-  auto compute_block = [&](int b, Block& t) {
+  auto compute_block = [&](int b, Block& t) __attribute__((always_inline)) {
     // the wave's V copy: rows past the context are zeroed (the pool may hold NaN there)
     const int live = t.ok ? min(16, kv_end - 16 * b) : 0;
 #pragma unroll
@@ -246,11 +319,12 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
   };
 
   // ---- stream the context: block b on wave b % W, one block of prefetch -----------------
-  const int nblk = (kv_end + 15) / 16;
+  const int b0 = t0 / 16;  // a partition starts on a block boundary
+  const int nblk = (kv_end + 15) / 16 - b0;
   const int nb = wave < nblk ? (nblk - wave + W - 1) / W : 0;
   if (nb > 0) {
     Block x, y;
-    int b = wave;
+    int b = b0 + wave;
     load_block(b, x);
     int i = 0;
     for (; i + 2 < nb; i += 2) {
@@ -303,9 +377,28 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
       den = fmaf(c, ml[w * ROWS + r], den);
     }
     const float o = den > 0.f ? num / den : 0.f;
-    reinterpret_cast<uint16_t*>(p.out)[((size_t)(a + t) * hq + (size_t)g * G + r % G) * D + d] =
-        (uint16_t)f32_to_bf16_rne(o);
+    if (DEC && nparts > 1) {  // a split partition: (o/l, m, l) for the reduce kernel
+      const size_t j = ((size_t)s * hq + (size_t)g * G + r % G) * p.max_parts + part;
+      p.ws_o[j * D + d] = o;
+      if (d == 0) {
+        p.ws_m[j] = mx;
+        p.ws_l[j] = den;
+      }
+    } else {
+      reinterpret_cast<uint16_t*>(p.out)[((size_t)(a + t) * hq + (size_t)g * G + r % G) * D + d] =
+          (uint16_t)f32_to_bf16_rne(o);
+    }
   }
+}
+
+template <int D, int G, int NT, bool E8>
+__global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeParams p) {
+  mq_body<D, G, NT, E8, false>(p);
+}
+
+template <int D, int G, bool E8>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams p) {
+  mq_body<D, G, 1, E8, true>(p);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -340,6 +433,32 @@ hipError_t launch_mq_dgn(const DecodeParams& p, int num_seqs, hipStream_t stream
   return hipGetLastError();
 }
 
+// The decode grid (KV head, partition, sequence), longest first with the snake order when whole
+// contexts are the units and the grid is resident at once (as for the vector decode kernel).
+template <int D, int G, bool E8>
+hipError_t launch_dec_dg(const DecodeParams& p, int num_seqs, hipStream_t stream) {
+  auto kernel = decode_mfma_kernel<D, G, E8>;
+  DecodeParams q = p;
+  q.snake = 0;
+  if (q.longest_first) {
+    static std::atomic<int> per_cu_cache{0};
+    int per_cu = per_cu_cache.load(std::memory_order_relaxed);
+    if (per_cu <= 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
+      per_cu_cache.store(per_cu, std::memory_order_relaxed);
+    const int cus = mq_device_cus();
+    if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu) q.snake = cus;
+  }
+  hipLaunchKernelGGL(kernel, dim3(p.num_kv_heads, p.max_parts, num_seqs), dim3(256), 0, stream, q);
+  return hipGetLastError();
+}
+
+template <int D, bool E8>
+hipError_t launch_dec_d(const DecodeParams& p, int gqa, int num_seqs, hipStream_t stream) {
+  if (gqa == 8) return launch_dec_dg<D, 8, E8>(p, num_seqs, stream);
+  if (gqa == 16) return launch_dec_dg<D, 16, E8>(p, num_seqs, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int D, int G, bool E8>
 hipError_t launch_mq_dg(const DecodeParams& p, int num_seqs, int max_q_len, hipStream_t stream) {
   if (max_q_len * G <= 16) return launch_mq_dgn<D, G, 1, E8>(p, num_seqs, stream);
@@ -361,6 +480,19 @@ hipError_t launch_mq_d(const DecodeParams& p, int gqa, int num_seqs, int max_q_l
 }  // namespace
 
 bool multiquery_applies(int gqa, int max_q_len) { return max_q_len >= 2 && max_q_len * gqa <= 32; }
+
+bool decode_mfma_applies(const DecodeParams& p, int kv_kind, int head_dim, int gqa) {
+  return p.cu_q == nullptr && (kv_kind == KV_BF16 || kv_kind == KV_E5M2) && (gqa == 8 || gqa == 16) &&
+         (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
+                              hipStream_t stream) {
+  const bool e8 = kv_kind == KV_E5M2;
+  if (head_dim == 128)
+    return e8 ? launch_dec_d<128, true>(p, gqa, num_seqs, stream) : launch_dec_d<128, false>(p, gqa, num_seqs, stream);
+  return e8 ? launch_dec_d<64, true>(p, gqa, num_seqs, stream) : launch_dec_d<64, false>(p, gqa, num_seqs, stream);
+}
 
 hipError_t launch_varlen_multiquery(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
                                     int max_q_len, hipStream_t stream) {

@@ -71,6 +71,12 @@ hipError_t static_workspace(void** ptr);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
                                 hipStream_t stream);
 
+// The decode calls (no packed rows) over a bf16 or E5M2 cache with 8 or 16 query heads per KV head:
+// the partition pass on MFMA (multiquery.hip), same grid, workspace and append as the vector one.
+bool decode_mfma_applies(const DecodeParams& p, int kv_kind, int head_dim, int gqa);
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs,
+                              hipStream_t stream);
+
 // Multi-token rows of a packed batch when every sequence has at most max_q_len tokens and
 // max_q_len * gqa <= 32 (speculative verification): one work-group streams each context once.
 bool multiquery_applies(int gqa, int max_q_len);

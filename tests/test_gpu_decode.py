@@ -225,7 +225,8 @@ def test_append_is_bit_identical_to_write_then_decode(idx, part):
     assert torch.equal(_bits(a.pk), _bits(b.pk)) and torch.equal(_bits(a.pv), _bits(b.pv))
 
 
-@pytest.mark.parametrize("dtype,D,G", [("e5m2", 128, 4), ("e5m2", 64, 8), ("bf16", 64, 2), ("f32", 128, 4)])
+@pytest.mark.parametrize("dtype,D,G", [("e5m2", 128, 4), ("e5m2", 64, 8), ("bf16", 64, 2), ("f32", 128, 4),
+                                         ("bf16", 128, 16), ("e5m2", 128, 8)])
 def test_append_edge_lengths_against_oracle(dtype, D, G):
     qd = "f32" if dtype == "f32" else "bf16"
     w = make_workload([1, 2, 16, 17, 32, 33, 300, 513, 0], num_q_heads=2 * G, num_kv_heads=2, head_dim=D, q_dtype=qd,

@@ -62,6 +62,13 @@ def test_long_context_split_kv_full_size_every_sequence():
     m = wsf[ob : ob + mb].view(torch.float32)[: n * hq * P].view(n, hq, P).cpu().numpy().astype(np.float64)
     l = wsf[ob + mb : ob + 2 * mb].view(torch.float32)[: n * hq * P].view(n, hq, P).cpu().numpy().astype(np.float64)
     qd = oracle.decode_storage(queries(w), "bf16")
+    # With 8 query heads per KV head the partition pass runs on MFMA: its probabilities enter the
+    # PV product and the row sum rounded to bf16 (unit roundoff u = 2^-9), the same rounded values
+    # in both.  Each weight's relative error is then at most u, so the sum's is too (lse off by at
+    # most -log2(1 - u)), and the normalised o moves by at most u / (1 - u) times the spread
+    # (max - min) of the values it averages.  The vector pass keeps them in fp32 (u = 0 here).
+    u = 2.0 ** -9 if w.gqa_group in (8, 16) else 0.0
+    lse_tol = -np.log2(1 - u)
     for s in range(n):
         L = int(w.context_lens[s])
         kk = oracle.decode_storage(oracle.gather_kv(pk, w.block_tables[s], L, 16), "bf16")
@@ -71,9 +78,14 @@ def test_long_context_split_kv_full_size_every_sequence():
         # than a fixed threshold, so the stored m may lag the true maximum; what is fixed is the
         # log-sum-exp m + log2(l) and the normalised o.
         lse_ref = (om[:, 0, :].T + np.log(ol[:, 0, :].T)) * np.log2(np.e)
-        np.testing.assert_allclose(m[s] + np.log2(l[s]), lse_ref, rtol=0, atol=1e-4)
+        np.testing.assert_allclose(m[s] + np.log2(l[s]), lse_ref, rtol=0, atol=1e-4 + lse_tol)
         assert np.all(m[s] <= om[:, 0, :].T * np.log2(np.e) + 1e-4)
-        assert np.abs(o[s] - oo[:, 0].transpose(1, 0, 2)).max() <= 1e-4, f"sequence {s} partials"
+        # per partition and dim: u / (1 - u) times the spread of that partition's values
+        ptp = np.stack([np.stack([np.ptp(vv[j * part : (j + 1) * part, h], axis=0) for j in range(P)])
+                        for h in range(w.num_kv_heads)])  # [Hkv][P][D]
+        bound = 1e-4 + u / (1 - u) * np.repeat(ptp, w.gqa_group, axis=0)  # [Hq][P][D]
+        err = np.abs(o[s] - oo[:, 0].transpose(1, 0, 2))
+        assert np.all(err <= bound), f"sequence {s} partials: max err {err.max():.2e}"
 
 
 def test_context_of_128k_tokens():
