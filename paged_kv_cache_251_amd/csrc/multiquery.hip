@@ -82,9 +82,8 @@ __device__ __forceinline__ const int32_t* table_of(const DecodeParams& p, int s)
 
 // E8: the cache holds E5M2 codes, widened to f16 as they are loaded; queries and probabilities
 // in f16 and the products on the f16 MFMA.  DEC: the decode calls (see above).
-template <int D, int G, int NT, bool E8, bool DEC>
+template <int D, int G, int NT, bool E8, bool DEC, int W = 4>
 __device__ __forceinline__ void mq_body(const DecodeParams& p) {
-  constexpr int W = 4;
   constexpr int ROWS = NT * 16;       // query rows of the work-group: row r = (token r / G, head r % G)
   constexpr int KS = D / 32;          // k-steps of the QK product
   constexpr int DT = D / 16;          // 16-dim output tiles
@@ -92,9 +91,10 @@ __device__ __forceinline__ void mq_body(const DecodeParams& p) {
   constexpr int VP = D + 16;          // row pitch of a wave's V copy (bf16): conflict-free transposed reads
   constexpr int VLD = 16 * CH / 64;   // 16-byte V chunks per lane per block
   constexpr int VWAVE = 16 * VP;      // bf16 per wave's V copy
-  constexpr int MERGE = W * ROWS * (D + 2);  // floats: each wave's o, m, l
-  constexpr int LDS_BYTES = (MERGE * 4 > W * VWAVE * 2 + 2 * kMaxRankedMq * 4) ? MERGE * 4
-                                                                               : W * VWAVE * 2 + 2 * kMaxRankedMq * 4;
+  // one wave (split partitions only) needs neither the merge nor the longest-first ranking
+  constexpr int MERGE_BYTES = W > 1 ? W * ROWS * (D + 2) * 4 : 0;  // each wave's o, m, l
+  constexpr int STREAM_BYTES = W * VWAVE * 2 + (W > 1 ? 2 * kMaxRankedMq * 4 : 0);
+  constexpr int LDS_BYTES = MERGE_BYTES > STREAM_BYTES ? MERGE_BYTES : STREAM_BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -104,7 +104,7 @@ __device__ __forceinline__ void mq_body(const DecodeParams& p) {
 
   int s = blockIdx.z, g = blockIdx.x;
   const int part = DEC ? blockIdx.y : 0;
-  if (p.longest_first) {
+  if (W > 1 && p.longest_first) {
     int* len = reinterpret_cast<int*>(lds + W * VWAVE * 2);
     const int2 u = longest_first_unit<64 * W>(p.context_lens, gridDim.z, gridDim.x, p.snake, len, len + kMaxRankedMq);
     s = u.x;
@@ -343,6 +343,42 @@ __device__ __forceinline__ void mq_body(const DecodeParams& p) {
     }
   }
 
+  if constexpr (W == 1) {
+    // one wave: its rows are the whole result; lane (lr, lg) holds dims dt*16 + 4 lg.. of row lr
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int r = j * 16 + lr, t = r / G;
+      if (t >= n) continue;
+      const float den = lacc[j][0];
+      if (DEC && nparts > 1) {  // a split partition: (o/l, m, l) for the reduce kernel
+        const size_t jj = ((size_t)s * hq + (size_t)g * G + r % G) * p.max_parts + part;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          float4 o;
+          o.x = den > 0.f ? oacc[j][dt][0] / den : 0.f;
+          o.y = den > 0.f ? oacc[j][dt][1] / den : 0.f;
+          o.z = den > 0.f ? oacc[j][dt][2] / den : 0.f;
+          o.w = den > 0.f ? oacc[j][dt][3] / den : 0.f;
+          *reinterpret_cast<float4*>(p.ws_o + jj * D + dt * 16 + 4 * lg) = o;
+        }
+        if (lg == 0) {
+          p.ws_m[jj] = m_run[j];
+          p.ws_l[jj] = den;
+        }
+      } else {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((size_t)(a + t) * hq + (size_t)g * G + r % G) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          uint32_t h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = f32_to_bf16_rne(den > 0.f ? oacc[j][dt][i] / den : 0.f);
+          *reinterpret_cast<uint2*>(orow + dt * 16 + 4 * lg) = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+        }
+      }
+    }
+    return;
+  }
+
   // ---- merge the waves: o (unnormalised), m, l per row through LDS ------------------------
   __syncthreads();  // the V copies are done with
   float* mo = reinterpret_cast<float*>(lds);          // [W][ROWS][D]
@@ -396,9 +432,10 @@ __global__ __launch_bounds__(256, 2) void varlen_multiquery_kernel(const DecodeP
   mq_body<D, G, NT, E8, false>(p);
 }
 
-template <int D, int G, bool E8>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(const DecodeParams p) {
-  mq_body<D, G, 1, E8, true>(p);
+// W waves per work-group: 4 on whole contexts, 1 per split partition (see launch_dec_dg)
+template <int D, int G, bool E8, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(const DecodeParams p) {
+  mq_body<D, G, 1, E8, true, W>(p);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -424,7 +461,8 @@ hipError_t launch_mq_dgn(const DecodeParams& p, int num_seqs, hipStream_t stream
     // snake order when the whole grid is resident at once (as for the decode kernel)
     static std::atomic<int> per_cu_cache{0};
     int per_cu = per_cu_cache.load(std::memory_order_relaxed);
-    if (per_cu <= 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
+    if (per_cu <= 0 &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
       per_cu_cache.store(per_cu, std::memory_order_relaxed);
     const int cus = mq_device_cus();
     if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu) q.snake = cus;
@@ -433,13 +471,22 @@ hipError_t launch_mq_dgn(const DecodeParams& p, int num_seqs, hipStream_t stream
   return hipGetLastError();
 }
 
-// The decode grid (KV head, partition, sequence), longest first with the snake order when whole
-// contexts are the units and the grid is resident at once (as for the vector decode kernel).
+// The decode grid (KV head, partition, sequence).  Whole contexts: 4 waves per work-group, longest
+// first with the snake order when the grid is resident at once (as for the vector decode kernel).
+// Split partitions: one wave per partition, whose rows are then the partition's result with no
+// merge through LDS; measured on 8 x 32768 tokens in 512-token partitions (G = 8), 181 us against
+// 188 us with 4 waves and 187 us with 2, while on whole contexts one wave per work-group is much
+// slower (fewer waves stream each context).
 template <int D, int G, bool E8>
 hipError_t launch_dec_dg(const DecodeParams& p, int num_seqs, hipStream_t stream) {
-  auto kernel = decode_mfma_kernel<D, G, E8>;
   DecodeParams q = p;
   q.snake = 0;
+  if (p.partition_tokens > 0) {
+    hipLaunchKernelGGL((decode_mfma_kernel<D, G, E8, 1>), dim3(p.num_kv_heads, p.max_parts, num_seqs), dim3(64), 0,
+                       stream, q);
+    return hipGetLastError();
+  }
+  auto kernel = decode_mfma_kernel<D, G, E8, 4>;
   if (q.longest_first) {
     static std::atomic<int> per_cu_cache{0};
     int per_cu = per_cu_cache.load(std::memory_order_relaxed);
@@ -448,7 +495,7 @@ hipError_t launch_dec_dg(const DecodeParams& p, int num_seqs, hipStream_t stream
     const int cus = mq_device_cus();
     if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu) q.snake = cus;
   }
-  hipLaunchKernelGGL(kernel, dim3(p.num_kv_heads, p.max_parts, num_seqs), dim3(256), 0, stream, q);
+  hipLaunchKernelGGL(kernel, dim3(p.num_kv_heads, 1, num_seqs), dim3(256), 0, stream, q);
   return hipGetLastError();
 }
 
