@@ -31,7 +31,8 @@ SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=unde
             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
             "-Xarch_host", "-g"]
 
-SOURCES = ["api.cpp", "block_manager.cpp", "scheduler.cpp", "cache_write.hip", "decode.hip", "varlen.hip", "multiquery.hip", "packed.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "scheduler.cpp", "cache_write.hip", "decode.hip", "reduce.hip", "varlen.hip",
+           "multiquery.hip", "packed.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

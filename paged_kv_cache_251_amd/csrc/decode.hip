@@ -44,85 +44,6 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(
   decode_body<KV, D, G, W>(p, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x, gridDim.z, sm_i, sm_f);
 }
 
-// Merge the partitions of every (sequence, query head) that was split: M = max_j m_j,
-// w_j = 2^(m_j - M) l_j, out = sum_j w_j o_j / sum_j w_j.  256 threads: NG groups of D/4
-// lanes take every NG-th partition, each lane 4 dims (one 16-byte load per partition row), with
-// the loop unrolled so that several partitions' loads are in flight; the groups then combine
-// through LDS.
-template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(const DecodeParams p) {
-  constexpr int LPR = D / 4;     // lanes per partition row
-  constexpr int NG = 256 / LPR;  // partition groups
-  const int h = blockIdx.x, s = blockIdx.y;
-  const int hq = gridDim.x;
-  const int sub = threadIdx.x % LPR, grp = threadIdx.x / LPR;
-  int qrow = s;
-  if (p.cu_q != nullptr) {
-    const int a = load_invariant(p.cu_q + s), b = load_invariant(p.cu_q + s + 1);
-    if (b - a != 1) return;
-    qrow = a;
-  }
-  int L = load_invariant(p.context_lens + s);
-  L = L < 0 ? 0 : L;
-  L = L > p.max_context_len ? p.max_context_len : L;
-  L = L > p.max_blocks_per_seq * 16 ? p.max_blocks_per_seq * 16 : L;
-  const int nparts = (L + p.partition_tokens - 1) / p.partition_tokens;
-  if (nparts <= 1) return;
-  const size_t base = ((size_t)s * hq + h) * p.max_parts;
-  __shared__ float sm_red[4];
-  __shared__ float sm_den[NG];
-  __shared__ float4 sm_num[NG][LPR];
-
-  float mx = -__builtin_inff();
-  for (int j = threadIdx.x; j < nparts; j += 256) mx = fmaxf(mx, p.ws_m[base + j]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((threadIdx.x & 63) == 0) sm_red[threadIdx.x >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(sm_red[0], sm_red[1]), fmaxf(sm_red[2], sm_red[3]));
-
-  float den = 0.f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float4* wo = reinterpret_cast<const float4*>(p.ws_o);
-#pragma unroll 4
-  for (int j = grp; j < nparts; j += NG) {
-    const float mj = p.ws_m[base + j];
-    const float w = (mj == -__builtin_inff()) ? 0.f : fast_exp2(mj - mx) * p.ws_l[base + j];
-    const float4 o = wo[(base + j) * LPR + sub];
-    den += w;
-    num.x = fmaf(w, o.x, num.x);
-    num.y = fmaf(w, o.y, num.y);
-    num.z = fmaf(w, o.z, num.z);
-    num.w = fmaf(w, o.w, num.w);
-  }
-  sm_num[grp][sub] = num;
-  if (sub == 0) sm_den[grp] = den;
-  __syncthreads();
-  if (threadIdx.x >= LPR) return;
-  float4 t = sm_num[0][sub];
-  float dsum = sm_den[0];
-#pragma unroll
-  for (int g = 1; g < NG; ++g) {
-    const float4 v = sm_num[g][sub];
-    t.x += v.x;
-    t.y += v.y;
-    t.z += v.z;
-    t.w += v.w;
-    dsum += sm_den[g];
-  }
-  const float o4[4] = {dsum > 0.f ? t.x / dsum : 0.f, dsum > 0.f ? t.y / dsum : 0.f, dsum > 0.f ? t.z / dsum : 0.f,
-                       dsum > 0.f ? t.w / dsum : 0.f};
-  const size_t orow = ((size_t)qrow * hq + h) * D + (size_t)sub * 4;
-  if constexpr (OUT_BF16) {
-    uint2 w2;
-    w2.x = f32_to_bf16_rne(o4[0]) | (f32_to_bf16_rne(o4[1]) << 16);
-    w2.y = f32_to_bf16_rne(o4[2]) | (f32_to_bf16_rne(o4[3]) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + orow) = w2;
-  } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + orow) = make_float4(o4[0], o4[1], o4[2], o4[3]);
-  }
-}
-
 // ---------------------------------------------------------------------------------------
 // Waves per work-group of the partition kernel.  A whole-context pass (one work-group per
 // (KV head, sequence)) takes 4: a CU holds two or more work-groups, so one that ends leaves the
@@ -240,21 +161,6 @@ hipError_t launch_decode_partitions(const DecodeParams& p, int kv_kind, int head
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
-                                hipStream_t stream) {
-  if (p.max_parts <= 1) return hipSuccess;
-  dim3 grid(num_q_heads, num_seqs);
-  if (head_dim == 128) {
-    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<128, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_reduce_kernel<128, false>), grid, dim3(256), 0, stream, p);
-  } else if (head_dim == 64) {
-    if (out_bf16) hipLaunchKernelGGL((decode_reduce_kernel<64, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_reduce_kernel<64, false>), grid, dim3(256), 0, stream, p);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------------------
 // Split-KV scratch of the entry point that allocates nothing: one array per GPU, held until the
