@@ -226,6 +226,10 @@ int32_t paged_attention_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
  * stay below 65536 in magnitude on these caches: a larger element overflows to inf, and the output
  * row of its (sequence, head) is then unspecified (zero or not finite, by path); every other head
  * and sequence is unaffected.
+ * Probabilities: with gqa_group 8 or 16 over a BF16 or FP8_E5M2 cache the dot products run on the
+ * matrix cores, and the probabilities enter the value product and the row sum rounded to bf16
+ * (f16 over FP8_E5M2), the same rounded values in both; the other shapes keep them in fp32 for a
+ * bf16 or f32 cache.  The partials m and l above follow the same rule.
  */
 pa_status_t paged_attention_decode(void* out, const void* query, const void* key_cache,
                                    const void* value_cache, const int32_t* block_tables,
