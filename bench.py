@@ -52,6 +52,13 @@ def row_bytes(w) -> int:
 LEAD_IN_CYCLES = 20_000_000
 
 
+def resident_lens(batches) -> str:
+    """Context-length range over every resident batch (the timed steps rotate over them)."""
+    lo = min(int(b.w.context_lens.min()) for b in batches)
+    hi = max(int(b.w.context_lens.max()) for b in batches)
+    return f"{lo}..{hi}"
+
+
 def lead_in(torch, stream) -> None:
     """Keep the GPU busy (a spin kernel, not timed) while the host queues the first steps, so the
     timed region opens on queued GPU work: what it measures is the device's time per step, not the
@@ -298,6 +305,7 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
             "num_kv_heads": w0.num_kv_heads,
             "head_dim": w0.head_dim,
             "block_size": w0.block_size,
+            "context_lens": resident_lens(batches),
             "partition_tokens": batches[0].resolved,
             "resident_batches": reps,
             "step": "slot mapping + cache write of every new token + paged_attention_varlen (one launch of "
@@ -306,6 +314,9 @@ def bench_varlen(args, pa, torch, np, to_dev, lib, stream, sh, check):
         "seq_steps_per_s": round(w0.num_seqs / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(step_bytes),
+        "kv_bytes_note": "mean over the timed steps, which rotate over the resident batches (independently "
+                         "seeded, of the same shape); each batch's own bytes are listed",
+        "kv_bytes_per_resident_batch": [int(b.kv_bytes) for b in batches],
         "roofline": {
             "kernel": "decode_partition_kernel (1-token rows of the packed batch)",
             "bound": "hbm",
@@ -371,6 +382,7 @@ def bench_multi_token(args, batches, timed, call, step, np):
             "num_kv_heads": w0.num_kv_heads,
             "head_dim": w0.head_dim,
             "block_size": w0.block_size,
+            "context_lens": resident_lens(batches),
             "resident_batches": reps,
             "step": "slot mapping + cache write of every new token + paged_attention_varlen (causal among "
                     "the new tokens)",
@@ -379,6 +391,9 @@ def bench_multi_token(args, batches, timed, call, step, np):
         "tokens_per_s": round(w0.total_q / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(step_bytes),
+        "kv_bytes_note": "mean over the timed steps, which rotate over the resident batches (independently "
+                         "seeded, of the same shape); each batch's own bytes are listed",
+        "kv_bytes_per_resident_batch": [int(b.kv_bytes) for b in batches],
         "roofline": {
             "kernel": "varlen_multiquery_kernel (every row; no decode launch)",
             "bound": "hbm",
@@ -531,7 +546,7 @@ def main():
             "num_kv_heads": w0.num_kv_heads,
             "head_dim": w0.head_dim,
             "block_size": w0.block_size,
-            "context_lens": f"{int(w0.context_lens.min())}..{int(w0.context_lens.max())}",
+            "context_lens": resident_lens(batches),
             "partition_tokens": batches[0].resolved,
             "resident_batches": reps,
             "step": (("one launch: slot mapping + " + ("quantising " if w0.kv_dtype in SCALED else "") +
@@ -543,6 +558,9 @@ def main():
         "seq_steps_per_s": round(seqs / (ms_step * 1e-3), 1),
         "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": int(step_bytes),
+        "kv_bytes_note": "mean over the timed steps, which rotate over the resident batches (independently "
+                         "seeded, of the same shape); each batch's own bytes are listed",
+        "kv_bytes_per_resident_batch": [int(b.kv_bytes) for b in batches],
         "unfused": None if not fused else {
             "ms_per_step": round(ms_unfused, 5),
             "GB_per_s": round(step_bytes / (ms_unfused * 1e-3) / 1e9, 2),
