@@ -352,17 +352,21 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, int bx, int b
       for (int k = 0; k < G; ++k) {
         float a = 0.f;
         if constexpr (Scaled<KV>::value) {
+          a = dot2_f16_first(qv[k][0], kh[0]);
 #pragma unroll
-          for (int j = 0; j < 2 * NDW; ++j) a = dot2_f16(qv[k][j], kh[j], a);
+          for (int j = 1; j < 2 * NDW; ++j) a = dot2_f16(qv[k][j], kh[j], a);
         } else if constexpr (KV == KV_F32) {
 #pragma unroll
           for (int j = 0; j < EPL; ++j) a = fmaf(as_f32(qv[k][j]), as_f32(kd[i][j]), a);
         } else if constexpr (KV == KV_BF16) {
+          a = dot2_bf16_first(qv[k][0], kd[i][0]);
 #pragma unroll
-          for (int j = 0; j < NDW; ++j) a = dot2_bf16(qv[k][j], kd[i][j], a);
+          for (int j = 1; j < NDW; ++j) a = dot2_bf16(qv[k][j], kd[i][j], a);
         } else {
+          a = dot2_f16_first(qv[k][0], e5m2_pair_lo(kd[i][0]));
+          a = dot2_f16(qv[k][1], e5m2_pair_hi(kd[i][0]), a);
 #pragma unroll
-          for (int j = 0; j < NDW; ++j) {
+          for (int j = 1; j < NDW; ++j) {
             a = dot2_f16(qv[k][2 * j], e5m2_pair_lo(kd[i][j]), a);
             a = dot2_f16(qv[k][2 * j + 1], e5m2_pair_hi(kd[i][j]), a);
           }

@@ -57,11 +57,14 @@ __device__ __forceinline__ float as_f32(uint32_t x) { return __builtin_bit_cast(
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
-  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), CTRL, 0xF, 0xF, false));
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(v), CTRL, 0xF, 0xF, true));
 }
+// Every control these two take (row_mirror, row_half_mirror, quad_perm, row_newbcast) gives each
+// lane a source in its own row, and all rows and banks are enabled, so no lane keeps `old`:
+// bound_ctrl lets the compiler leave it unset instead of zeroing a register first.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
 constexpr int DPP_ROW_MIRROR = 0x140;
@@ -316,6 +319,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+// The same products with no accumulator (the first step of a chain).  From a zero start the
+// compiler picks the accumulating encoding and first zeroes its destination with a move; the
+// three-operand form takes the 0 as an inline constant, one instruction instead of two.
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float dot2_f16_first(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // Two binary32 -> f16x2, each rounded to nearest even.
