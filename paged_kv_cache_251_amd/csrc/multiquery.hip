@@ -267,12 +267,18 @@ __device__ __forceinline__ void mq_body(const DecodeParams& p) {
   };
 
   auto compute_block = [&](int b, Block& t) __attribute__((always_inline)) {
-    // the wave's V copy: rows past the context are zeroed (the pool may hold NaN there)
+    // the wave's V copy.  Rows past the context must read as zeros (the pool may hold NaN there);
+    // only a context's last block has such rows, so every block is copied as loaded and that one
+    // then has its dead rows overwritten, each lane rewriting its own slots (its later store
+    // wins).  A per-lane select on every block compiled to four divergent branches, and a select
+    // under a wave-uniform branch to register copies before the stores.
     const int live = t.ok ? min(16, kv_end - 16 * b) : 0;
 #pragma unroll
-    for (int u = 0; u < VLD; ++u) {
-      const int key = (lane + 64 * u) / CH;
-      *reinterpret_cast<uint4*>(vs + v_lds[u]) = key < live ? t.v[u] : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < VLD; ++u) *reinterpret_cast<uint4*>(vs + v_lds[u]) = t.v[u];
+    if (live < 16) {
+#pragma unroll
+      for (int u = 0; u < VLD; ++u)
+        if ((lane + 64 * u) / CH >= live) *reinterpret_cast<uint4*>(vs + v_lds[u]) = make_uint4(0, 0, 0, 0);
     }
     const bool whole = t.ok && 16 * b + 16 <= lim_min;
 #pragma unroll
