@@ -35,8 +35,8 @@ def _static(b, partition, out, max_context_len=None):
     return st
 
 
-def _case(lens, partition, seed, kv_dtype="bf16"):
-    w = make_workload(lens, num_q_heads=32, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype=kv_dtype,
+def _case(lens, partition, seed, kv_dtype="bf16", num_q_heads=32):
+    w = make_workload(lens, num_q_heads=num_q_heads, num_kv_heads=8, head_dim=128, q_dtype="bf16", kv_dtype=kv_dtype,
                       seed=seed)
     b = DeviceBatch(w)
     need = pa.workspace_size(w.num_seqs, w.num_kv_heads, w.gqa_group, w.head_dim, w.max_context_len, partition)
@@ -69,6 +69,20 @@ def test_static_scratch_whole_context_and_e5m2():
         ref = b.decode(part)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"partition {part} differs"
+
+
+def test_static_scratch_on_the_matrix_core_decode_path():
+    # 8 query heads per KV head: the partition pass runs on MFMA; a split call, then a smaller one
+    # and a whole-context one on the same array
+    for lens, part, seed in (([5000, 17, 1200], 64, 74), ([700, 1, 300], 256, 75), ([2100, 9], 0, 76)):
+        w, b, need = _case(lens, part, seed=seed, num_q_heads=64)
+        assert need <= LIMIT, need
+        print(f"[no-alloc] G8 lens {w.context_lens.tolist()}, partition {part}", flush=True)
+        got = torch.full_like(b.q, float("nan"))
+        assert _static(b, part, got) == 0, pa.lib().pa_last_error().decode()
+        ref = b.decode(part)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"G8 partition {part} differs"
 
 
 def test_static_scratch_refuses_a_split_larger_than_the_array():
