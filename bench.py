@@ -72,7 +72,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, help="workload 1-7 (1-4 decode, 5 packed prefill + decode, 6 speculative verification of 4 tokens, "
+    ap.add_argument("--config", type=int, default=2, help="workload 1-9 (1-4 decode, 5 packed prefill + decode, 6 speculative verification of 4 tokens, "
                     "7 decode over an INT8 pool, 8 over a scaled FP8 E4M3 pool, 9 the packed step over an E5M2 "
                     "pool)")
     ap.add_argument("--replicas", type=int, default=0, help="resident batches to rotate (0: enough for >= 1.2 GB)")
