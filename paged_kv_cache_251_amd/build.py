@@ -2,6 +2,10 @@
 
     python -m paged_kv_cache_251_amd.build              # libpagedattn.so
     python -m paged_kv_cache_251_amd.build --sanitize   # libpagedattn_san.so
+    python -m paged_kv_cache_251_amd.build --define NAME=VALUE ... --out PATH
+        # a comparison build with the sources' tuning switches set (e.g.
+        # PA_DECODE_MFMA_WIDE_GROUPS=0: the vector decode pass for every group size), written to
+        # PATH and loaded with PA_LIBRARY=PATH; its objects go to a folder of their own
 
 The sanitized library has its host code (the C ABI, the block manager, the scheduler) built with
 AddressSanitizer and UndefinedBehaviorSanitizer (host side only; the kernels are built as usual).
@@ -57,10 +61,10 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
-    out = os.path.join(OBJ_SAN if sanitize else OBJ, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, sanitize: bool = False, defines=(), obj=None) -> str:
+    out = os.path.join(obj or (OBJ_SAN if sanitize else OBJ), os.path.splitext(src)[0] + ".o")
     extra = SANITIZE if sanitize and src in HOST_SOURCES else []
-    cmd = [_hipcc(), *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [_hipcc(), *FLAGS, *extra, *(f"-D{d}" for d in defines), "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -72,11 +76,21 @@ def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
     return out
 
 
-def build(verbose: bool = False, sanitize: bool = False) -> str:
-    os.makedirs(OBJ_SAN if sanitize else OBJ, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False, defines=(), out=None) -> str:
+    """Compile and link the library.  `defines` (NAME=VALUE strings) and `out` make a comparison
+    build: it never replaces the plain library and keeps its objects apart."""
+    if defines and not out:
+        raise ValueError("a build with defines needs an output path of its own")
+    obj = None
+    if out:
+        import hashlib
+
+        tag = hashlib.sha1(" ".join(sorted(defines)).encode()).hexdigest()[:10]
+        obj = os.path.join(PKG, f"_build_{tag}")
+    os.makedirs(obj or (OBJ_SAN if sanitize else OBJ), exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), SOURCES))
-    lib = LIB_SAN if sanitize else LIB
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize, defines, obj), SOURCES))
+    lib = os.path.abspath(out) if out else (LIB_SAN if sanitize else LIB)
     tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -113,4 +127,12 @@ def sanitizer_env(base=None) -> dict:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true", dest="verbose")
+    ap.add_argument("--sanitize", action="store_true")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE")
+    ap.add_argument("--out", default=None, metavar="PATH")
+    a = ap.parse_args()
+    print(build(verbose=a.verbose, sanitize=a.sanitize, defines=a.define, out=a.out))
