@@ -313,7 +313,7 @@ pa_status_t prepare_decode(const char* fn, pa::DecodeParams& p, void* out, const
   p.max_parts = static_cast<int32_t>(parts);
   p.scale_log2 = scale * 1.4426950408889634f;
   // longest-first only pays when whole contexts are the work units (see decode.hip)
-  p.longest_first = PA_LONGEST_FIRST && parts <= 1 && num_seqs <= 1024;
+  p.longest_first = PA_LONGEST_FIRST && parts <= 1 && num_seqs <= pa::kLongestFirstMaxSeqs;
   return PA_OK;
 }
 

@@ -62,6 +62,8 @@ __global__ __launch_bounds__(64 * W) void decode_partition_kernel(
 #ifndef PA_DECODE_MFMA_WIDE_GROUPS
 #define PA_DECODE_MFMA_WIDE_GROUPS 1
 #endif
+static_assert(kLongestFirstMaxSeqs <= kMaxRankedSeqs, "the ranking buffer holds every ranked sequence");
+
 #ifndef PA_DECODE_WAVES_WHOLE
 #define PA_DECODE_WAVES_WHOLE 4
 #endif
@@ -120,6 +122,9 @@ static hipError_t launch_parts_kv_d_g(const DecodeParams& p, int num_seqs, hipSt
         q.snake = cus;
         q.resident = cus * per_cu;
       }
+      // a decode call (every sequence one row) whose units do not all fit: plain grid order, the
+      // ranking would cost more than the order gains (packed batches: the kernel counts its rows)
+      if (p.cu_q == nullptr && (long long)num_seqs * p.num_kv_heads > (long long)q.resident) q.longest_first = 0;
     }
     hipLaunchKernelGGL(kernel, grid, dim3(64 * W), 0, stream, q);
   } else {

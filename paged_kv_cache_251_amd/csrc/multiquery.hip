@@ -44,6 +44,7 @@ typedef short mq_v4i16_t __attribute__((ext_vector_type(4)));
 
 constexpr float kTauMq = 8.0f;
 constexpr int kMaxRankedMq = 1024;
+static_assert(kLongestFirstMaxSeqs <= kMaxRankedMq, "the ranking buffer holds every ranked sequence");
 
 typedef __attribute__((ext_vector_type(8))) _Float16 mq_f16x8_t;
 typedef __attribute__((ext_vector_type(4))) _Float16 mq_f16x4_t;
@@ -461,17 +462,21 @@ template <int D, int G, int NT, bool E8>
 hipError_t launch_mq_dgn(const DecodeParams& p, int num_seqs, hipStream_t stream) {
   auto kernel = varlen_multiquery_kernel<D, G, NT, E8>;
   DecodeParams q = p;
-  q.longest_first = num_seqs <= kMaxRankedMq ? 1 : 0;
+  q.longest_first = num_seqs <= kLongestFirstMaxSeqs ? 1 : 0;
   q.snake = 0;
   if (q.longest_first) {
-    // snake order when the whole grid is resident at once (as for the decode kernel)
+    // longest first with the snake order when the whole grid is resident at once (as for the
+    // decode kernel); otherwise the plain grid order
     static std::atomic<int> per_cu_cache{0};
     int per_cu = per_cu_cache.load(std::memory_order_relaxed);
     if (per_cu <= 0 &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
       per_cu_cache.store(per_cu, std::memory_order_relaxed);
     const int cus = mq_device_cus();
-    if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu) q.snake = cus;
+    if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu)
+      q.snake = cus;
+    else
+      q.longest_first = 0;
   }
   hipLaunchKernelGGL(kernel, dim3(p.num_kv_heads, 1, num_seqs), dim3(256), 0, stream, q);
   return hipGetLastError();
@@ -499,7 +504,10 @@ hipError_t launch_dec_dg(const DecodeParams& p, int num_seqs, hipStream_t stream
     if (per_cu <= 0 && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) == hipSuccess)
       per_cu_cache.store(per_cu, std::memory_order_relaxed);
     const int cus = mq_device_cus();
-    if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu) q.snake = cus;
+    if (cus > 0 && per_cu > 0 && (long long)num_seqs * p.num_kv_heads <= (long long)cus * per_cu)
+      q.snake = cus;
+    else
+      q.longest_first = 0;  // not all resident: plain grid order (see kLongestFirstMaxSeqs)
   }
   hipLaunchKernelGGL(kernel, dim3(p.num_kv_heads, 1, num_seqs), dim3(256), 0, stream, q);
   return hipGetLastError();

@@ -71,6 +71,14 @@ hipError_t static_workspace(void** ptr);
 hipError_t launch_decode_reduce(const DecodeParams& p, bool out_bf16, int head_dim, int num_q_heads, int num_seqs,
                                 hipStream_t stream);
 
+// Longest-first order (every work-group ranks the batch's sequences by length) is used up to this
+// many sequences, and by the decode and multi-query launchers only when every unit of the grid is
+// resident at once, where the snake order pairs long and short contexts on each CU.  The ranking
+// costs each work-group O(n^2 / threads); measured on bf16 decode batches (4 query heads per KV
+// head) against the plain grid order: 61.1 against 64.9 us at 64 sequences (resident), but 65.8
+// against 63.5 at 128, 140 against 116 at 256, and 2131 against 146 us at 1024.
+constexpr int kLongestFirstMaxSeqs = 128;
+
 // The decode calls (no packed rows) over a bf16 or E5M2 cache with 8 or 16 query heads per KV head:
 // the partition pass on MFMA (multiquery.hip), same grid, workspace and append as the vector one.
 bool decode_mfma_applies(const DecodeParams& p, int kv_kind, int head_dim, int gqa);

@@ -122,8 +122,15 @@ static hipError_t launch_packed_d(const DecodeParams& p, int gqa, int num_seqs, 
   return hipErrorInvalidValue;
 }
 
+// Every work-group of the two-role kernel ranks the batch's sequences (O(n^2 / threads) each), so
+// large batches take the two kernels back to back instead.  Measured with 4 prefill chunks (32
+// query / 8 KV heads): one launch 241.8 against 300.4 us with 128 decode rows, 408.3 against 463.7
+// with 252, but 894.9 against 799.6 with 508.
+constexpr int kPackedMaxSeqs = 256;
+
 bool packed_step_applies(const DecodeParams& p, int num_seqs, int max_q_len) {
-  return p.max_parts <= 1 && num_seqs <= kMaxScheduledSeqs && num_seqs <= kMaxRankedSeqs && max_q_len >= 2;
+  return p.max_parts <= 1 && num_seqs <= kPackedMaxSeqs && num_seqs <= kMaxScheduledSeqs &&
+         num_seqs <= kMaxRankedSeqs && max_q_len >= 2;
 }
 
 hipError_t launch_packed_step(const DecodeParams& p, int kv_kind, int head_dim, int gqa, int num_seqs, int total_q,
