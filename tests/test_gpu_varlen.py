@@ -84,6 +84,19 @@ def test_varlen_more_sequences_than_the_ranked_limit():
     assert_close(out_f64(_varlen(b, 0), "bf16"), _oracle_rows(w, pk, pv), "bf16", "1030 sequences")
 
 
+def test_varlen_packed_batch_above_the_one_launch_limit():
+    """300 sequences with prefill chunks among them: above the two-role kernel's 256, the decode
+    and prefill kernels run back to back, the decode rows in plain grid order (above 128)."""
+    rng = np.random.default_rng(79)
+    n_new = np.ones(300, np.int64)
+    n_new[[0, 7, 150, 299]] = [40, 3, 129, 17]
+    lens = n_new + rng.integers(0, 400, size=300)
+    w = make_workload(lens, q_lens=n_new, num_q_heads=8, num_kv_heads=2, head_dim=128, q_dtype="bf16", seed=79)
+    b = DeviceBatch(w)
+    pk, pv = oracle_pools(w)
+    assert_close(out_f64(_varlen(b, 0), "bf16"), _oracle_rows(w, pk, pv), "bf16", "300 sequences")
+
+
 def test_varlen_block_permutation_and_packing_order_are_bit_identical():
     w = _mixed(5, 4, 128)
     b = DeviceBatch(w)
